@@ -1,0 +1,180 @@
+"""Seeded synthetic workloads: layer shapes, schemes and input generators.
+
+This module only draws random inputs of the right shapes and value
+distributions. It holds none of the method's arithmetic (no decode, no
+product), so both the HIP path and the CPU oracle can take their inputs
+from it without sharing any computation.
+
+Packed format (one quantized linear layer, out x in):
+  codes      [out, in/g, M]   uint8 (B = 8) or uint16 (B = 16), m fastest
+  codebooks  [M, 2**B, g]     float16
+  scales     [out]            float16
+  x          [batch, in]      float16
+
+Value distributions: codes uniform over [0, 2**B); codebook entries drawn
+from N(0, 0.02) in float64 then rounded to float16; scales U(0.5, 1.5)
+rounded to float16; x standard normal rounded to float16. The random
+generator is numpy's PCG64 (default_rng), drawn in the order codes,
+codebooks, scales, x, so that the batch size changes only x.
+
+Shapes follow the linear layers of Llama-2-7B (hidden 4096, MLP 11008) and
+Llama-2-70B (hidden 8192, MLP 28672, grouped-query k/v of 1024 rows); the
+schemes are the pages' "2x8" (two 8-bit codebooks) and "1x16" (one 16-bit
+codebook) with codeword length g = 8, plus a g = 16 variant of 1x16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Scheme:
+    """An additive codebook scheme: M codebooks of 2**B codewords of length g."""
+    M: int
+    B: int
+    g: int
+
+    @property
+    def name(self) -> str:
+        return f"{self.M}x{self.B}g{self.g}"
+
+    @property
+    def code_dtype(self):
+        return np.uint8 if self.B <= 8 else np.uint16
+
+
+S2x8 = Scheme(2, 8, 8)
+S1x16 = Scheme(1, 16, 8)
+S1x16g16 = Scheme(1, 16, 16)
+
+
+@dataclass(frozen=True)
+class Layer:
+    name: str
+    out_features: int
+    in_features: int
+    scheme: Scheme
+    seed: int
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A named set of layers and the batch sizes each is run at."""
+    name: str
+    index: int
+    layers: Tuple[Layer, ...]
+    batches: Tuple[int, ...]
+    description: str = ""
+
+
+_LLAMA2_7B = (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096),
+              ("o", 4096, 4096), ("gate", 11008, 4096), ("up", 11008, 4096),
+              ("down", 4096, 11008))
+_LLAMA2_70B = (("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192),
+               ("o", 8192, 8192), ("gate", 28672, 8192), ("up", 28672, 8192),
+               ("down", 8192, 28672))
+
+
+def _layers(index: int, shapes, scheme: Scheme) -> Tuple[Layer, ...]:
+    return tuple(Layer(n, o, i, scheme, 1000 * index + li)
+                 for li, (n, o, i) in enumerate(shapes))
+
+
+def _gemm_layers(index: int) -> Tuple[Layer, ...]:
+    out = []
+    li = 0
+    for scheme in (S1x16g16, S2x8):
+        for n, o, i in (("up", 11008, 4096), ("down", 4096, 11008)):
+            out.append(Layer(f"{n}_{scheme.name}", o, i, scheme, 1000 * index + li))
+            li += 1
+    return tuple(out)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w for w in (
+        Workload("single_2x8_512x1024", 1,
+                 (Layer("single", 512, 1024, S2x8, 1000),), (1,),
+                 "one 512x1024 layer, scheme 2x8 g8, batch 1"),
+        Workload("llama2_7b_2x8", 2, _layers(2, _LLAMA2_7B, S2x8), (1,),
+                 "Llama-2-7B linear layers, scheme 2x8 g8, batch 1"),
+        Workload("llama2_7b_1x16", 3, _layers(3, _LLAMA2_7B, S1x16), (1, 4, 8),
+                 "Llama-2-7B linear layers, scheme 1x16 g8, batch 1/4/8"),
+        Workload("llama2_70b_1x16", 4, _layers(4, _LLAMA2_70B, S1x16), (1,),
+                 "Llama-2-70B linear layers, scheme 1x16 g8, batch 1"),
+        Workload("gemm_mlp", 5, _gemm_layers(5), (16, 128, 2048),
+                 "MLP-shaped layers (11008x4096, 4096x11008), schemes 1x16 g16 "
+                 "and 2x8 g8, batch 16/128/2048"),
+    )
+}
+
+
+@dataclass
+class LayerData:
+    layer: Layer
+    codes: np.ndarray       # [out, in/g, M] uint8/uint16
+    codebooks: np.ndarray   # [M, 2**B, g] float16
+    scales: np.ndarray      # [out] float16
+
+    @property
+    def scheme(self) -> Scheme:
+        return self.layer.scheme
+
+
+def make_packed(out_features: int, in_features: int, scheme: Scheme, seed: int,
+                codebook_std: float = 0.02,
+                scale_range: Tuple[float, float] = (0.5, 1.5)) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.random.Generator]:
+    """Draw (codes, codebooks, scales) and return the generator for x."""
+    if in_features % scheme.g:
+        raise ValueError("in_features must be a multiple of the group size")
+    rng = np.random.default_rng(seed)
+    J = in_features // scheme.g
+    codes = rng.integers(0, 2 ** scheme.B, size=(out_features, J, scheme.M),
+                         dtype=scheme.code_dtype)
+    codebooks = rng.normal(0.0, codebook_std,
+                           size=(scheme.M, 2 ** scheme.B, scheme.g)).astype(np.float16)
+    scales = rng.uniform(scale_range[0], scale_range[1], size=out_features).astype(np.float16)
+    return codes, codebooks, scales, rng
+
+
+def make_layer(layer: Layer) -> LayerData:
+    codes, codebooks, scales, _ = make_packed(layer.out_features, layer.in_features,
+                                              layer.scheme, layer.seed)
+    return LayerData(layer, codes, codebooks, scales)
+
+
+def make_x(layer: Layer, batch: int) -> np.ndarray:
+    """x for a layer at a batch size: the draw that follows the layer's weights."""
+    _, _, _, rng = make_packed(layer.out_features, layer.in_features, layer.scheme,
+                               layer.seed)
+    return rng.standard_normal((batch, layer.in_features)).astype(np.float16)
+
+
+def make_x_only(batch: int, in_features: int, seed: int) -> np.ndarray:
+    """A standalone fp16 activation batch (for cases with no layer attached)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((batch, in_features)).astype(np.float16)
+
+
+def small_case(out_features: int, in_features: int, scheme: Scheme, batch: int,
+               seed: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """A small random layer plus x, for parity at sizes the oracle finishes fast."""
+    codes, codebooks, scales, rng = make_packed(out_features, in_features, scheme, seed)
+    x = rng.standard_normal((batch, in_features)).astype(np.float16)
+    return codes, codebooks, scales, x
+
+
+def workload_bytes(layer: Layer, batch: int) -> Dict[str, int]:
+    """Byte counts of the packed tensors and activations of one layer."""
+    s = layer.scheme
+    J = layer.in_features // s.g
+    code_bytes = layer.out_features * J * s.M * np.dtype(s.code_dtype).itemsize
+    return {
+        "codes": code_bytes,
+        "codebooks": s.M * (2 ** s.B) * s.g * 2,
+        "scales": layer.out_features * 2,
+        "x": batch * layer.in_features * 2,
+        "y": batch * layer.out_features * 2,
+    }
