@@ -1,0 +1,189 @@
+"""ctypes binding of the HIP library (libaqlm_mi355x.so).
+
+Argument marshalling only: torch tensors are checked for device, dtype,
+shape, contiguity and alignment, and their device pointers and the current
+HIP stream are handed to the C entry points. Every step of the computation
+runs in the library's kernels. There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libaqlm_mi355x.so")
+
+AQLM_OK = 0
+STATUS_NAMES = {0: "AQLM_OK", 1: "AQLM_ERR_NULL", 2: "AQLM_ERR_SHAPE", 3: "AQLM_ERR_SCHEME",
+                4: "AQLM_ERR_ALIGN", 5: "AQLM_ERR_BATCH", 6: "AQLM_ERR_HIP"}
+EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemm", "aqlm_status_string",
+                    "aqlm_abi_version")
+ABI_VERSION = 1
+SCHEMES = {(2, 8, 8): "2x8", (1, 16, 8): "1x16", (1, 16, 16): "1x16g16"}
+
+
+class AqlmLayerStruct(ctypes.Structure):
+    """Mirror of struct aqlm_layer in include/aqlm.h."""
+    _fields_ = [
+        ("out_features", ctypes.c_int64),
+        ("in_features", ctypes.c_int64),
+        ("num_codebooks", ctypes.c_int32),
+        ("nbits", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("codebooks", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+    ]
+
+
+class AqlmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built library (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP library not found at {LIB_PATH}; build it with "
+            "`python -m additive_codebook_matmul_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lp = ctypes.POINTER(AqlmLayerStruct)
+    lib.aqlm_dequant.argtypes = [lp, ctypes.c_void_p, ctypes.c_void_p]
+    lib.aqlm_dequant.restype = ctypes.c_int
+    for name in ("aqlm_gemv", "aqlm_gemm"):
+        fn = getattr(lib, name)
+        fn.argtypes = [lp, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    lib.aqlm_status_string.argtypes = [ctypes.c_int]
+    lib.aqlm_status_string.restype = ctypes.c_char_p
+    lib.aqlm_abi_version.argtypes = []
+    lib.aqlm_abi_version.restype = ctypes.c_int
+    if lib.aqlm_abi_version() != ABI_VERSION:
+        raise RuntimeError("libaqlm_mi355x.so ABI version mismatch; rebuild the library")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().aqlm_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != AQLM_OK:
+        raise AqlmError(status, status_string(status))
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class AqlmLayer:
+    """A quantized linear layer held as device tensors in the packed format.
+
+    codes      [out, in/g, M]  torch.uint8 (B = 8) or torch.int16/uint16 bits (B = 16)
+    codebooks  [M, 2**B, g]    torch.float16
+    scales     [out]           torch.float16
+    """
+
+    def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor):
+        if codes.dim() != 3 or codebooks.dim() != 3 or scales.dim() != 1:
+            raise ValueError("codes [out, in/g, M], codebooks [M, 2**B, g], scales [out]")
+        out, J, M = codes.shape
+        Mc, ncode, g = codebooks.shape
+        if Mc != M or scales.shape[0] != out:
+            raise ValueError("codes, codebooks and scales disagree in shape")
+        if ncode < 2 or ncode & (ncode - 1):
+            raise ValueError("codebook size must be a power of two")
+        B = ncode.bit_length() - 1
+        want = torch.uint8 if B == 8 else (torch.int16, torch.uint16)
+        if (B == 8 and codes.dtype != torch.uint8) or (B == 16 and codes.dtype not in want):
+            raise ValueError(f"codes dtype {codes.dtype} does not match {B}-bit codes")
+        if codebooks.dtype != torch.float16 or scales.dtype != torch.float16:
+            raise ValueError("codebooks and scales must be float16")
+        for t in (codes, codebooks, scales):
+            if not t.is_cuda:
+                raise ValueError("all tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+        if not (codes.device == codebooks.device == scales.device):
+            raise ValueError("all tensors must be on one device")
+        self.codes, self.codebooks, self.scales = codes, codebooks, scales
+        self.out_features, self.in_features = int(out), int(J * g)
+        self.M, self.B, self.g = int(M), int(B), int(g)
+        self.device = codes.device
+        self._struct = AqlmLayerStruct(self.out_features, self.in_features, self.M, self.B, self.g,
+                                       0, codes.data_ptr(), codebooks.data_ptr(),
+                                       scales.data_ptr())
+
+    @property
+    def scheme(self) -> str:
+        return SCHEMES.get((self.M, self.B, self.g), f"{self.M}x{self.B}g{self.g}")
+
+    def _check_x(self, x: torch.Tensor) -> torch.Tensor:
+        if x.dim() != 2 or x.shape[1] != self.in_features:
+            raise ValueError(f"x must be [batch, {self.in_features}]")
+        if x.dtype != torch.float16 or not x.is_contiguous() or x.device != self.device:
+            raise ValueError("x must be a contiguous float16 tensor on the layer's device")
+        return x
+
+    def dequant(self, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        lib = load_library()
+        if out is None:
+            out = torch.empty((self.out_features, self.in_features), dtype=torch.float16,
+                              device=self.device)
+        elif (out.shape != (self.out_features, self.in_features) or out.dtype != torch.float16
+              or not out.is_contiguous() or out.device != self.device):
+            raise ValueError("out must be a contiguous float16 [out, in] tensor on the device")
+        with torch.cuda.device(self.device):
+            _check(lib.aqlm_dequant(ctypes.byref(self._struct), out.data_ptr(),
+                                    _stream_handle(self.device)))
+        return out
+
+    def _product(self, fn_name: str, x: torch.Tensor, out: Optional[torch.Tensor]) -> torch.Tensor:
+        lib = load_library()
+        x = self._check_x(x)
+        batch = x.shape[0]
+        if out is None:
+            out = torch.empty((batch, self.out_features), dtype=torch.float16, device=self.device)
+        elif (out.shape != (batch, self.out_features) or out.dtype != torch.float16
+              or not out.is_contiguous() or out.device != self.device):
+            raise ValueError("out must be a contiguous float16 [batch, out] tensor on the device")
+        with torch.cuda.device(self.device):
+            _check(getattr(lib, fn_name)(ctypes.byref(self._struct), x.data_ptr(), batch,
+                                         out.data_ptr(), _stream_handle(self.device)))
+        return out
+
+    def gemv(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """y = x . W^T for 1..8 activation rows (codebook-lookup path)."""
+        return self._product("aqlm_gemv", x, out)
+
+    def gemm(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """y = x . W^T for any number of activation rows (matrix-core path)."""
+        return self._product("aqlm_gemm", x, out)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        """Pick the lookup path for <= 8 rows and the matrix-core path above."""
+        return self.gemv(x) if x.shape[0] <= 8 else self.gemm(x)
+
+
+def raw_call(fn_name: str, struct: AqlmLayerStruct, *args) -> int:
+    """Call an entry point with a hand-built descriptor (for boundary tests)."""
+    lib = load_library()
+    return getattr(lib, fn_name)(ctypes.byref(struct), *args)

@@ -1,0 +1,101 @@
+// C entry points: argument validation on the host, then kernel launch on the
+// caller's stream. Nothing here allocates or synchronises.
+#include <limits.h>
+
+#include "../../include/aqlm.h"
+#include "aqlm_internal.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate the layer descriptor and fill the internal description.
+int check_layer(const aqlm_layer *layer, aqlm::LayerDesc *d) {
+  if (!layer) return AQLM_ERR_NULL;
+  if (!layer->codes || !layer->codebooks || !layer->scales) return AQLM_ERR_NULL;
+  const int M = layer->num_codebooks, B = layer->nbits, g = layer->group_size;
+  aqlm::Scheme s;
+  if (M == 2 && B == 8 && g == 8)
+    s = aqlm::Scheme::k2x8;
+  else if (M == 1 && B == 16 && g == 8)
+    s = aqlm::Scheme::k1x16;
+  else if (M == 1 && B == 16 && g == 16)
+    s = aqlm::Scheme::k1x16g16;
+  else
+    return AQLM_ERR_SCHEME;
+  if (layer->reserved != 0) return AQLM_ERR_SHAPE;
+  if (layer->out_features < 1 || layer->in_features < 1) return AQLM_ERR_SHAPE;
+  if (layer->in_features % g) return AQLM_ERR_SHAPE;
+  // Kernels index rows and columns with 32-bit integers.
+  if (layer->out_features > INT_MAX / 2 || layer->in_features > INT_MAX / 2) return AQLM_ERR_SHAPE;
+  if (!aligned16(layer->codes) || !aligned16(layer->codebooks) || !aligned16(layer->scales))
+    return AQLM_ERR_ALIGN;
+  d->out = layer->out_features;
+  d->in = layer->in_features;
+  d->groups = layer->in_features / g;
+  d->scheme = s;
+  d->codes = layer->codes;
+  d->books = layer->codebooks;
+  d->scales = layer->scales;
+  return AQLM_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? AQLM_OK : AQLM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int aqlm_abi_version(void) { return AQLM_ABI_VERSION; }
+
+const char *aqlm_status_string(int status) {
+  switch (status) {
+    case AQLM_OK: return "ok";
+    case AQLM_ERR_NULL: return "a required pointer is NULL";
+    case AQLM_ERR_SHAPE: return "invalid shape: need out >= 1, in >= 1, in % group_size == 0, "
+                                "sizes below 2^30 and reserved == 0";
+    case AQLM_ERR_SCHEME: return "unsupported scheme: (M, B, g) must be (2, 8, 8), (1, 16, 8) "
+                                 "or (1, 16, 16)";
+    case AQLM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case AQLM_ERR_BATCH: return "batch outside the entry point's range";
+    case AQLM_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}
+
+int aqlm_dequant(const aqlm_layer *layer, uint16_t *W, void *stream) {
+  aqlm::LayerDesc d;
+  const int st = check_layer(layer, &d);
+  if (st != AQLM_OK) return st;
+  if (!W) return AQLM_ERR_NULL;
+  if (!aligned16(W)) return AQLM_ERR_ALIGN;
+  return from_hip(aqlm::launch_dequant(d, W, static_cast<hipStream_t>(stream)));
+}
+
+int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
+              void *stream) {
+  aqlm::LayerDesc d;
+  const int st = check_layer(layer, &d);
+  if (st != AQLM_OK) return st;
+  if (batch < 0 || batch > 8) return AQLM_ERR_BATCH;
+  if (batch == 0) return AQLM_OK;
+  if (!x || !y) return AQLM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return AQLM_ERR_ALIGN;
+  return from_hip(aqlm::launch_gemv(d, x, (int)batch, y, static_cast<hipStream_t>(stream)));
+}
+
+int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
+              void *stream) {
+  aqlm::LayerDesc d;
+  const int st = check_layer(layer, &d);
+  if (st != AQLM_OK) return st;
+  if (batch < 0 || batch > (int64_t)INT_MAX / 2) return AQLM_ERR_BATCH;
+  if (batch == 0) return AQLM_OK;
+  if (!x || !y) return AQLM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return AQLM_ERR_ALIGN;
+  // grid.y holds the activation-row tiles
+  if ((batch + 63) / 64 > 65535) return AQLM_ERR_BATCH;
+  return from_hip(aqlm::launch_gemm(d, x, batch, y, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

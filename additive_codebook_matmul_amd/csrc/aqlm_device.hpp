@@ -1,0 +1,118 @@
+// Device helpers: fp16 bit conversions, the exact group decode, dot products
+// and wavefront reductions for gfx950 (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "aqlm_internal.hpp"
+
+namespace aqlm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte accesses that bypass cache retention (data used once).
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt16(void *p, const uint4 &w) {
+  u32x4_t v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, static_cast<u32x4_t *>(p));
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+// float32 -> float16, round to nearest even, subnormals kept, overflow to inf
+// (v_cvt_f16_f32 under the default rounding and denormal modes).
+__device__ __forceinline__ uint32_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// Two fp16 products accumulated into float32: c + a.lo*b.lo + a.hi*b.hi.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+
+__device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b, float c) {
+  c = dot2(a.x, b.x, c);
+  c = dot2(a.y, b.y, c);
+  c = dot2(a.z, b.z, c);
+  c = dot2(a.w, b.w, c);
+  return c;
+}
+
+// Packed fp16 add of two codewords (8 halves each): the on-chip tile form used
+// by the matrix-core product, where the row scale is applied in the epilogue.
+__device__ __forceinline__ uint32_t hadd2(uint32_t a, uint32_t b) {
+  half2_t r = __builtin_bit_cast(half2_t, a) + __builtin_bit_cast(half2_t, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint4 hadd8(const uint4 &a, const uint4 &b) {
+  return make_uint4(hadd2(a.x, b.x), hadd2(a.y, b.y), hadd2(a.z, b.z), hadd2(a.w, b.w));
+}
+
+// Pins a float32 value in a register: the optimiser may not fold the
+// operation that produced it into a later one. Without it, fp16(a * s) is
+// compiled to v_fma_mixlo_f16(a, s, +0), which rounds the exact product once
+// to fp16 instead of to fp32 first, and turns -0 * s into +0.
+__device__ __forceinline__ float materialize(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Exact decode of one weight from its codewords' halves: float32 sum in
+// ascending codebook order starting from the first codeword, float32 scale,
+// one round to float16.
+__device__ __forceinline__ uint32_t decode1(uint32_t c0, float s) {
+  return f2h(materialize(materialize(h2f(c0)) * s));
+}
+__device__ __forceinline__ uint32_t decode2(uint32_t c0, uint32_t c1, float s) {
+  const float sum = materialize(materialize(h2f(c0)) + materialize(h2f(c1)));
+  return f2h(materialize(sum * s));
+}
+
+// Decode a packed pair of halves (one 32-bit word of each codeword).
+__device__ __forceinline__ uint32_t decode_word2(uint32_t a, uint32_t b, float s) {
+  return decode2(a & 0xFFFFu, b & 0xFFFFu, s) | (decode2(a >> 16, b >> 16, s) << 16);
+}
+__device__ __forceinline__ uint32_t decode_word1(uint32_t a, float s) {
+  return decode1(a & 0xFFFFu, s) | (decode1(a >> 16, s) << 16);
+}
+
+// DPP row/bank controls (gfx9 family).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF, bool BOUND_CTRL = false>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, BANK_MASK,
+                                         BOUND_CTRL));
+}
+
+// Sum over the 64 lanes of a wavefront in a fixed order; the total is valid in
+// lane 63 (other lanes hold partial sums).
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  v += dpp<kDppRowBcast15, 0xA>(v);
+  v += dpp<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+}  // namespace aqlm

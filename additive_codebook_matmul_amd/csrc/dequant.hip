@@ -1,0 +1,103 @@
+// Dequantization: W[o][j*g + k] for every group (o, j), bit-exact to the
+// decode rule (float32 codeword sum in codebook order, float32 row scale,
+// one round to nearest-even float16).
+//
+// The kernel writes 2*out*in bytes and reads 2 bytes of codes per g weights,
+// so it is bound by HBM writes. One thread decodes one group: two code bytes
+// (2x8) or one 16-bit code (1x16) in, g float16 (16 or 32 bytes) out, stored
+// with 16-byte vector stores that are contiguous across the wavefront. The
+// 2x8 codebooks (8 KiB) are staged in LDS; the 1x16 codebooks (1 or 2 MiB)
+// are read through the L2 cache.
+#include "aqlm_device.hpp"
+
+namespace aqlm {
+namespace {
+
+constexpr int kBlock = 256;
+
+__global__ __launch_bounds__(kBlock) void dequant_2x8_kernel(
+    const uint16_t *__restrict__ codes, const uint16_t *__restrict__ books,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ W, int64_t groups_per_row,
+    int64_t total_groups) {
+  __shared__ uint4 lds_books[2 * 256];  // [m][code] -> 8 halves
+  const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
+  for (int i = threadIdx.x; i < 2 * 256; i += kBlock) lds_books[i] = gbooks[i];
+  __syncthreads();
+
+  uint4 *W4 = reinterpret_cast<uint4 *>(W);
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x; gid < total_groups;
+       gid += stride) {
+    const int64_t o = gid / groups_per_row;
+    const uint32_t pair = codes[gid];  // low byte: codebook 0, high byte: codebook 1
+    const uint4 a = lds_books[pair & 0xFF];
+    const uint4 b = lds_books[256 + (pair >> 8)];
+    const float s = h2f(scales[o]);
+    uint4 w;
+    w.x = decode_word2(a.x, b.x, s);
+    w.y = decode_word2(a.y, b.y, s);
+    w.z = decode_word2(a.z, b.z, s);
+    w.w = decode_word2(a.w, b.w, s);
+    store_nt16(W4 + gid, w);
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kBlock) void dequant_1x16_kernel(
+    const uint16_t *__restrict__ codes, const uint16_t *__restrict__ books,
+    const uint16_t *__restrict__ scales, uint16_t *__restrict__ W, int64_t groups_per_row,
+    int64_t total_groups) {
+  constexpr int V = G / 8;  // 16-byte vectors per codeword
+  const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
+  uint4 *W4 = reinterpret_cast<uint4 *>(W);
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x; gid < total_groups;
+       gid += stride) {
+    const int64_t o = gid / groups_per_row;
+    const uint32_t c = codes[gid];
+    const float s = h2f(scales[o]);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const uint4 a = gbooks[(int64_t)c * V + v];
+      uint4 w;
+      w.x = decode_word1(a.x, s);
+      w.y = decode_word1(a.y, s);
+      w.z = decode_word1(a.z, s);
+      w.w = decode_word1(a.w, s);
+      store_nt16(W4 + gid * V + v, w);
+    }
+  }
+}
+
+int grid_for(int64_t work) {
+  int64_t blocks = (work + kBlock - 1) / kBlock;
+  const int64_t cap = 256 * 64;  // enough waves to fill 256 CUs many times over
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const LayerDesc &L, uint16_t *W, hipStream_t stream) {
+  const int64_t total = L.out * L.groups;
+  const uint16_t *codes = static_cast<const uint16_t *>(L.codes);
+  const int grid = grid_for(total);
+  switch (L.scheme) {
+    case Scheme::k2x8:
+      hipLaunchKernelGGL(dequant_2x8_kernel, dim3(grid), dim3(kBlock), 0, stream, codes, L.books,
+                         L.scales, W, L.groups, total);
+      break;
+    case Scheme::k1x16:
+      hipLaunchKernelGGL(dequant_1x16_kernel<8>, dim3(grid), dim3(kBlock), 0, stream, codes,
+                         L.books, L.scales, W, L.groups, total);
+      break;
+    case Scheme::k1x16g16:
+      hipLaunchKernelGGL(dequant_1x16_kernel<16>, dim3(grid), dim3(kBlock), 0, stream, codes,
+                         L.books, L.scales, W, L.groups, total);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace aqlm

@@ -1,0 +1,129 @@
+/*
+ * aqlm.h - C ABI of the MI355X (gfx950) library for additive multi-codebook
+ * quantized linear layers (AQLM).
+ *
+ * The operation. A linear layer y = x . W^T whose weight matrix W [out, in]
+ * is stored as sums of learned codebook vectors: every weight vector is the
+ * sum of one codeword from each of M codebooks ("Additive quantization that
+ * actually survives one-bit weights", section "What it does"; "AQLM
+ * (additive / multi-codebook quantization)", field "Activation scheme").
+ * Activations stay float16; only the weights are quantized ("AQLM (additive
+ * / multi-codebook quantization)", field "Bits").
+ *
+ * Packed format (all arrays dense, row-major, little-endian):
+ *   codes      [out][in/g][M]   uint8 when B == 8, uint16 when B == 16; an
+ *                               entry is an unsigned codeword index < 2^B
+ *   codebooks  [M][2^B][g]      float16 bit patterns
+ *   scales     [out]            float16 bit patterns, one per output row
+ * Group j of output row o covers input columns j*g .. j*g+g-1, and
+ *   W[o][j*g+k] = fp16_rne( float(scales[o]) *
+ *                           (float(C_0[c_0][k]) + ... + float(C_{M-1}[c_{M-1}][k])) )
+ * with c_m = codes[o][j][m], the float32 sum taken in ascending m starting
+ * from the m = 0 codeword, a float32 multiply, and one round to nearest-even
+ * float16 (subnormals kept, overflow to infinity). The pages leave the
+ * group-to-column map, the scale and the rounding unstated; this is the
+ * library's reading of them.
+ *
+ * Supported schemes (M, B, g): (2, 8, 8) "2x8", (1, 16, 8) "1x16" and
+ * (1, 16, 16) "1x16 g16" -- the 8- and 16-dimensional codebook schemes of
+ * "Additive quantization that actually survives one-bit weights", sections
+ * "Key highlights" and "Caveats". Any in_features that is a multiple of g
+ * is accepted.
+ *
+ * Pointers. Every array pointer is a DEVICE pointer on the current HIP
+ * device; codes, codebooks, scales, x, y and W must each be 16-byte aligned.
+ * The caller owns every buffer: the library allocates nothing, frees
+ * nothing and keeps no pointer after a call returns. Outputs must not alias
+ * inputs.
+ *
+ * Streams and errors. `stream` is a hipStream_t (NULL = the default stream).
+ * Each entry point validates its arguments on the host, then enqueues its
+ * kernels on `stream` and returns without synchronising; buffers must stay
+ * alive until that stream's work is done. On a validation failure nothing is
+ * enqueued and a status below is returned. A launch failure reported by the
+ * HIP runtime returns AQLM_ERR_HIP. Faults inside a kernel surface at the
+ * caller's next synchronisation. All entry points are reentrant and keep no
+ * state. Results are deterministic: the same inputs give bit-identical
+ * outputs on every call.
+ */
+#ifndef AQLM_MI355X_H
+#define AQLM_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AQLM_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define AQLM_API __attribute__((visibility("default")))
+#else
+#define AQLM_API
+#endif
+
+typedef enum aqlm_status {
+  AQLM_OK = 0,
+  AQLM_ERR_NULL = 1,   /* a required pointer is NULL */
+  AQLM_ERR_SHAPE = 2,  /* out < 1, in < 1, in % g != 0, or a size overflows */
+  AQLM_ERR_SCHEME = 3, /* (M, B, g) is not a supported scheme */
+  AQLM_ERR_ALIGN = 4,  /* a pointer is not 16-byte aligned */
+  AQLM_ERR_BATCH = 5,  /* batch outside the entry point's range */
+  AQLM_ERR_HIP = 6     /* the HIP runtime reported an error at launch */
+} aqlm_status;
+
+/* One quantized layer: sizes plus device pointers to the packed arrays. */
+typedef struct aqlm_layer {
+  int64_t out_features;      /* rows of W, >= 1 */
+  int64_t in_features;       /* columns of W, >= 1, multiple of group_size */
+  int32_t num_codebooks;     /* M */
+  int32_t nbits;             /* B: codebook size is 2^B */
+  int32_t group_size;        /* g: codeword length */
+  int32_t reserved;          /* must be 0 */
+  const void *codes;         /* device, [out][in/g][M] uint8 (B=8) / uint16 (B=16) */
+  const uint16_t *codebooks; /* device, [M][2^B][g] float16 bits */
+  const uint16_t *scales;    /* device, [out] float16 bits */
+} aqlm_layer;
+
+/*
+ * aqlm_dequant: materialise W [out][in] float16 (row-major) from the packed
+ * layer, bit-exact to the decode rule above. W is written in full; it is
+ * the dequantize-to-float16 step that precedes a dense float16 matrix
+ * product ("AQLM (additive / multi-codebook quantization)", notes).
+ */
+AQLM_API int aqlm_dequant(const aqlm_layer *layer, uint16_t *W, void *stream);
+
+/*
+ * aqlm_gemv: y[b][o] = sum_i x[b][i] * W[o][i] for b < batch, 1 <= batch <= 8,
+ * without materialising W: codes are streamed once and every group is
+ * decoded by codebook lookup inside the kernel (the token-generation path
+ * of "AQLM (additive / multi-codebook quantization)", field "Kernels").
+ * x is [batch][in] float16, y is [batch][out] float16 (round to nearest
+ * from a float32 accumulation). batch == 0 is a no-op returning AQLM_OK.
+ */
+AQLM_API int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
+              uint16_t *y, void *stream);
+
+/*
+ * aqlm_gemm: the same product for any batch >= 1 (batch == 0: no-op). Tiles
+ * of W are decoded on chip and fed to float16 matrix-core (MFMA)
+ * instructions with float32 accumulation; W is never written to memory
+ * ("AQLM (additive / multi-codebook quantization)", notes: dequantize to
+ * float16, then a float16 matrix-engine product). x is [batch][in], y is
+ * [batch][out], both float16.
+ */
+AQLM_API int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
+              uint16_t *y, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+AQLM_API const char *aqlm_status_string(int status);
+
+/* AQLM_ABI_VERSION of the built library. */
+AQLM_API int aqlm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQLM_MI355X_H */

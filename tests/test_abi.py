@@ -1,0 +1,121 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point,
+and rejects bad arguments before anything is launched (no GPU needed: every
+call here fails validation or is a batch == 0 no-op, so no kernel starts)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from additive_codebook_matmul_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aqlm.h")
+
+FAKE = 0x10000      # a 16-byte aligned address that is never dereferenced
+MISALIGNED = 0x10008
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"AQLM_API\s+[\w\s\*]*?\b(aqlm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(_lib.EXPORTED_SYMBOLS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.aqlm_abi_version() == _lib.ABI_VERSION
+
+
+def test_struct_layout_matches_header():
+    # int64, int64, 4 x int32, 3 pointers
+    assert ctypes.sizeof(_lib.AqlmLayerStruct) == 8 + 8 + 16 + 3 * 8
+    assert _lib.AqlmLayerStruct.codes.offset == 32
+
+
+def test_status_strings():
+    for st in range(7):
+        assert _lib.status_string(st)
+    assert _lib.status_string(99) == "unknown status"
+    assert _lib.status_string(0) == "ok"
+
+
+def _layer(M=2, B=8, g=8, out=64, n_in=128, codes=FAKE, books=FAKE, scales=FAKE, reserved=0):
+    return _lib.AqlmLayerStruct(out, n_in, M, B, g, reserved, codes, books, scales)
+
+
+ENTRY = {
+    "aqlm_dequant": lambda s, x, b, y: _lib.raw_call("aqlm_dequant", s, y, None),
+    "aqlm_gemv": lambda s, x, b, y: _lib.raw_call("aqlm_gemv", s, x, b, y, None),
+    "aqlm_gemm": lambda s, x, b, y: _lib.raw_call("aqlm_gemm", s, x, b, y, None),
+}
+
+
+@pytest.mark.parametrize("fn", sorted(ENTRY))
+def test_null_layer_pointer(fn):
+    lib = _lib.load_library()
+    f = getattr(lib, fn)
+    if fn == "aqlm_dequant":
+        assert f(None, FAKE, None) == 1
+    else:
+        assert f(None, FAKE, 1, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("fn", sorted(ENTRY))
+@pytest.mark.parametrize("case,status", [
+    (dict(codes=0), 1), (dict(books=0), 1), (dict(scales=0), 1),
+    (dict(M=3), 3), (dict(B=12), 3), (dict(g=4), 3), (dict(M=1, B=8), 3), (dict(M=2, B=16), 3),
+    (dict(out=0), 2), (dict(n_in=0), 2), (dict(n_in=100), 2), (dict(out=-5), 2),
+    (dict(reserved=1), 2), (dict(out=1 << 40), 2),
+    (dict(M=1, B=16, g=16, n_in=136), 2),
+    (dict(codes=MISALIGNED), 4), (dict(books=MISALIGNED), 4), (dict(scales=MISALIGNED), 4),
+])
+def test_layer_validation(fn, case, status):
+    s = _layer(**case)
+    assert ENTRY[fn](s, FAKE, 1, FAKE) == status
+
+
+@pytest.mark.parametrize("fn", sorted(ENTRY))
+def test_output_pointer_validation(fn):
+    s = _layer()
+    assert ENTRY[fn](s, FAKE, 1, 0) == 1
+    assert ENTRY[fn](s, FAKE, 1, MISALIGNED) == 4
+
+
+@pytest.mark.parametrize("fn", ["aqlm_gemv", "aqlm_gemm"])
+def test_input_pointer_and_batch_validation(fn):
+    s = _layer()
+    assert ENTRY[fn](s, 0, 1, FAKE) == 1
+    assert ENTRY[fn](s, MISALIGNED, 1, FAKE) == 4
+    assert ENTRY[fn](s, FAKE, -1, FAKE) == 5
+    # batch == 0 is a no-op that launches nothing, even with unusable pointers
+    assert ENTRY[fn](s, 0, 0, 0) == 0
+
+
+def test_batch_limits():
+    s = _layer()
+    assert ENTRY["aqlm_gemv"](s, FAKE, 9, FAKE) == 5
+    assert ENTRY["aqlm_gemm"](s, FAKE, 1 << 40, FAKE) == 5
+
+
+def test_binding_rejects_cpu_tensors_without_calling_the_library():
+    import torch
+    codes = torch.zeros((4, 2, 2), dtype=torch.uint8)
+    books = torch.zeros((2, 256, 8), dtype=torch.float16)
+    scales = torch.zeros(4, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        _lib.AqlmLayer(codes, books, scales)
+    with pytest.raises(ValueError):
+        _lib.AqlmLayer(codes.to(torch.int16), books, scales)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        _lib.load_library()

@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Decoded weights (aqlm_dequant) must match bit for bit; products (aqlm_gemv,
+aqlm_gemm) must lie within 1e-2 * sum_i |x_i w_i| of the float64 oracle for
+every output, and within the tighter 1e-3 gate. Sizes: small ragged layers
+that span several tiles and a tail, and every layer of the five workloads at
+full size (the 70B-shaped layers on sampled rows, the 2048-row products on
+sampled activation rows).
+"""
+import functools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from additive_codebook_matmul_amd import AqlmLayer, workloads as WL
+from gpu_util import (assert_bit_exact, assert_product, bits, dev_layer, dev_x, device,
+                      to_dev_codes)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SCHEMES = {"2x8": WL.S2x8, "1x16": WL.S1x16, "1x16g16": WL.S1x16g16}
+
+# (out, groups): single row/group, ragged rows and groups, multiples of the
+# 16-byte code chunk (8 groups) with and without row tails, several tiles.
+SMALL_SHAPES = [(1, 1), (7, 5), (64, 8), (255, 13), (300, 64), (33, 172), (513, 24), (257, 9)]
+
+
+def _small(scheme, out, J, batch, seed):
+    return WL.small_case(out, J * scheme.g, scheme, batch, seed)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _announce():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    yield
+
+
+# ---------------------------------------------------------------------------
+# small, ragged
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("sname", list(SCHEMES))
+@pytest.mark.parametrize("out,J", SMALL_SHAPES)
+def test_small_dequant_bit_exact(sname, out, J):
+    s = SCHEMES[sname]
+    codes, books, scales, _ = _small(s, out, J, 1, seed=out * 131 + J)
+    w = dev_layer(codes, books, scales).dequant()
+    assert_bit_exact(w.cpu().numpy(), oracle.decode(codes, books, scales), f"{sname} {out}x{J}")
+
+
+@pytest.mark.parametrize("sname", list(SCHEMES))
+@pytest.mark.parametrize("out,J", SMALL_SHAPES)
+def test_small_gemv(sname, out, J):
+    s = SCHEMES[sname]
+    codes, books, scales, x = _small(s, out, J, 8, seed=out * 17 + J)
+    layer = dev_layer(codes, books, scales)
+    for batch in range(1, 9):
+        y = layer.gemv(dev_x(x[:batch]))
+        y_ref, bound = oracle.forward(x[:batch], codes, books, scales)
+        assert_product(y, y_ref, bound, f"gemv {sname} {out}x{J} b{batch}")
+
+
+@pytest.mark.parametrize("sname", list(SCHEMES))
+@pytest.mark.parametrize("out,J", SMALL_SHAPES)
+def test_small_gemm(sname, out, J):
+    s = SCHEMES[sname]
+    codes, books, scales, x = _small(s, out, J, 130, seed=out * 23 + J)
+    layer = dev_layer(codes, books, scales)
+    for batch in (1, 5, 64, 65, 130):
+        y = layer.gemm(dev_x(x[:batch]))
+        y_ref, bound = oracle.forward(x[:batch], codes, books, scales)
+        assert_product(y, y_ref, bound, f"gemm {sname} {out}x{J} b{batch}")
+
+
+# ---------------------------------------------------------------------------
+# golden values on the GPU
+# ---------------------------------------------------------------------------
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "hand_worked_groups.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_golden_hand_worked(case):
+    M, B, g = case["M"], case["B"], case["g"]
+    books = np.zeros((M, 2 ** B, g), dtype=np.float16)
+    for m, rows in case["codebook_rows"].items():
+        for c, vals in rows.items():
+            books[int(m), int(c)] = np.asarray(vals, dtype=np.float16)
+    codes = np.asarray(case["codes"], dtype=np.uint8 if B == 8 else np.uint16)
+    scales = np.asarray(case["scales"], dtype=np.float16)
+    x = np.asarray(case["x"], dtype=np.float16)
+    layer = dev_layer(codes, books, scales)
+    w = layer.dequant().cpu().numpy()
+    if "expected_w_bits" in case:
+        exp = np.array([[int(h, 16) for h in r] for r in case["expected_w_bits"]], dtype=np.uint16)
+    else:
+        exp = bits(np.asarray(case["expected_w"], dtype=np.float16))
+    assert np.array_equal(bits(w), exp)
+    expected_y = np.asarray(case["expected_y"], dtype=np.float64)
+    for fn in (layer.gemv, layer.gemm):
+        y = fn(dev_x(x)).cpu().numpy().astype(np.float64)
+        assert np.array_equal(y, expected_y), (fn.__name__, y, expected_y)
+
+
+def _rounding_cases():
+    with open(os.path.join(GOLDEN, "rounding_cases.json")) as f:
+        return [c for c in json.load(f)["cases"] if len(c["codewords"]) in (1, 2)]
+
+
+@pytest.mark.parametrize("case", _rounding_cases(), ids=lambda c: c["name"])
+def test_golden_rounding_dequant(case):
+    """The golden single-weight decodes, placed in a real 2x8 or 1x16 layer."""
+    cw = [int(h, 16) for h in case["codewords"]]
+    if len(cw) == 2:
+        books = np.zeros((2, 256, 8), dtype=np.uint16)
+        books[0, 7, 3], books[1, 9, 3] = cw
+        codes = np.array([[[7, 9]]], dtype=np.uint8)
+    else:
+        books = np.zeros((1, 65536, 8), dtype=np.uint16)
+        books[0, 40000, 3] = cw[0]
+        codes = np.array([[[40000]]], dtype=np.uint16)
+    scales = np.array([int(case["scale"], 16)], dtype=np.uint16).view(np.float16)
+    w = dev_layer(codes, books.view(np.float16), scales).dequant()
+    assert int(bits(w)[0, 3]) == int(case["expected"], 16), case["name"]
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size
+# ---------------------------------------------------------------------------
+@functools.lru_cache(maxsize=4)
+def _layer_data(wname, lname):
+    wl = WL.WORKLOADS[wname]
+    layer = next(l for l in wl.layers if l.name == lname)
+    return layer, WL.make_layer(layer)
+
+
+def _sample_rows(out, n=1024, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, out - 2, out - 1],
+                                     rng.choice(out, size=min(out, n), replace=False)]))
+    return rows[(rows >= 0) & (rows < out)]
+
+
+LAYER_IDS = [(w.name, l.name) for w in WL.WORKLOADS.values() for l in w.layers]
+BIG = {"llama2_70b_1x16"}  # oracle on sampled rows
+
+
+@pytest.mark.parametrize("wname,lname", LAYER_IDS, ids=lambda v: str(v))
+def test_workload_dequant_bit_exact(wname, lname):
+    layer, d = _layer_data(wname, lname)
+    gl = dev_layer(d.codes, d.codebooks, d.scales)
+    w = gl.dequant()
+    if wname in BIG:
+        rows = _sample_rows(layer.out_features)
+        w_rows = w[torch.from_numpy(rows).to(device())].cpu().numpy()
+        ref = oracle.decode_rows(d.codes, d.codebooks, d.scales, rows)
+        assert_bit_exact(w_rows, ref, f"{wname}/{lname} sampled rows")
+    else:
+        assert_bit_exact(w.cpu().numpy(), oracle.decode(d.codes, d.codebooks, d.scales),
+                         f"{wname}/{lname}")
+    del w
+    torch.cuda.empty_cache()
+
+
+GEMV_IDS = [(w.name, l.name, b) for w in WL.WORKLOADS.values() if w.index <= 4
+            for l in w.layers for b in w.batches]
+
+
+@pytest.mark.parametrize("wname,lname,batch", GEMV_IDS, ids=lambda v: str(v))
+def test_workload_gemv(wname, lname, batch):
+    layer, d = _layer_data(wname, lname)
+    x = WL.make_x(layer, batch)
+    y = dev_layer(d.codes, d.codebooks, d.scales).gemv(dev_x(x)).cpu().numpy()
+    if wname in BIG:
+        rows = _sample_rows(layer.out_features)
+        y_ref, bound = oracle.forward_rows(x, d.codes, d.codebooks, d.scales, rows)
+        assert_product(y[:, rows], y_ref, bound, f"{wname}/{lname} b{batch}")
+    else:
+        y_ref, bound = oracle.forward(x, d.codes, d.codebooks, d.scales)
+        assert_product(y, y_ref, bound, f"{wname}/{lname} b{batch}")
+
+
+GEMM_IDS = [(l.name, b) for l in WL.WORKLOADS["gemm_mlp"].layers
+            for b in WL.WORKLOADS["gemm_mlp"].batches]
+
+
+@pytest.mark.parametrize("lname,batch", GEMM_IDS, ids=lambda v: str(v))
+def test_workload_gemm(lname, batch):
+    layer, d = _layer_data("gemm_mlp", lname)
+    x = WL.make_x(layer, batch)
+    y = dev_layer(d.codes, d.codebooks, d.scales).gemm(dev_x(x)).cpu().numpy()
+    toks = np.arange(batch) if batch <= 128 else np.unique(np.concatenate(
+        [[0, batch - 1], np.random.default_rng(1).choice(batch, 62, replace=False)]))
+    y_ref, bound = oracle.forward(x[toks], d.codes, d.codebooks, d.scales)
+    assert_product(y[toks], y_ref, bound, f"gemm {lname} b{batch}")
+
+
+# ---------------------------------------------------------------------------
+# probes the loose tolerance cannot replace
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("sname,out,n_in", [("2x8", 4096, 4096), ("1x16", 4096, 11008),
+                                            ("1x16g16", 1000, 2048), ("2x8", 300, 520)])
+def test_one_hot_probes(sname, out, n_in):
+    """x = e_i returns column i of W: the lookup path to within one float16 ulp,
+    exactly for the decode-then-dot order (first/last column of groups, row tail)."""
+    s = SCHEMES[sname]
+    codes, books, scales, _ = WL.small_case(out, n_in, s, 1, seed=out + n_in)
+    layer = dev_layer(codes, books, scales)
+    w_ref = oracle.decode(codes, books, scales).astype(np.float32)
+    cols = np.unique(np.array([0, s.g - 1, s.g, n_in // 2, n_in // 2 + 1, n_in - s.g,
+                               n_in - 2, n_in - 1]))
+    for fn in (layer.gemv, layer.gemm):
+        for c0 in range(0, len(cols), 8):
+            cc = cols[c0:c0 + 8]
+            x = np.zeros((len(cc), n_in), dtype=np.float16)
+            x[np.arange(len(cc)), cc] = 1
+            y = fn(dev_x(x)).cpu().numpy().astype(np.float32)
+            ref = w_ref[:, cc].T
+            ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float32)
+            assert np.all(np.abs(y - ref) <= ulp), (fn.__name__, sname, cc)
+
+
+@pytest.mark.parametrize("sname", list(SCHEMES))
+def test_deterministic(sname):
+    s = SCHEMES[sname]
+    codes, books, scales, x = WL.small_case(2000, 2048, s, 64, seed=5)
+    layer = dev_layer(codes, books, scales)
+    for fn, xb in ((layer.gemv, x[:8]), (layer.gemm, x)):
+        a = bits(fn(dev_x(xb)))
+        b = bits(fn(dev_x(xb)))
+        assert np.array_equal(a, b), fn.__name__
+
+
+@pytest.mark.parametrize("sname", list(SCHEMES))
+def test_outputs_stay_in_bounds(sname):
+    """Canary words after y and W stay untouched."""
+    s = SCHEMES[sname]
+    out, n_in = 300, 13 * s.g
+    codes, books, scales, x = WL.small_case(out, n_in, s, 8, seed=7)
+    layer = dev_layer(codes, books, scales)
+    canary = np.float16(-12345.0)
+    ybuf = torch.full((8 * out + 64,), float(canary), dtype=torch.float16, device=device())
+    for fn in ("gemv", "gemm"):
+        y = ybuf[: 8 * out].view(8, out)
+        getattr(layer, fn)(dev_x(x), out=y)
+        assert torch.all(ybuf[8 * out:] == float(canary)), fn
+    wbuf = torch.full((out * n_in + 64,), float(canary), dtype=torch.float16, device=device())
+    layer.dequant(out=wbuf[: out * n_in].view(out, n_in))
+    assert torch.all(wbuf[out * n_in:] == float(canary))
+
+
+def test_zero_batch_is_noop():
+    codes, books, scales, x = WL.small_case(16, 64, WL.S2x8, 1, seed=1)
+    layer = dev_layer(codes, books, scales)
+    y = torch.full((0, 16), 1.0, dtype=torch.float16, device=device())
+    assert layer.gemv(dev_x(x[:0])).shape == (0, 16)
+    assert layer.gemm(dev_x(x[:0])).shape == (0, 16)
