@@ -5,6 +5,8 @@ include/aqlm.h); `AqlmLayer` is its thin torch-facing binding. Importing the
 package does not load the library; the first call does, and fails loudly if
 it has not been built.
 """
-from ._lib import AqlmError, AqlmLayer, load_library, library_path, status_string  # noqa: F401
+from ._lib import (AqlmError, AqlmLayer, gemv_batched, library_path, load_library,  # noqa: F401
+                   status_string)
 
-__all__ = ["AqlmLayer", "AqlmError", "load_library", "library_path", "status_string"]
+__all__ = ["AqlmLayer", "AqlmError", "gemv_batched", "load_library", "library_path",
+           "status_string"]

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_PKG_DIR, "libaqlm_mi355x.so")
 AQLM_OK = 0
 STATUS_NAMES = {0: "AQLM_OK", 1: "AQLM_ERR_NULL", 2: "AQLM_ERR_SHAPE", 3: "AQLM_ERR_SCHEME",
                 4: "AQLM_ERR_ALIGN", 5: "AQLM_ERR_BATCH", 6: "AQLM_ERR_HIP"}
-EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemm", "aqlm_status_string",
-                    "aqlm_abi_version")
+EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemv_batched", "aqlm_gemm",
+                    "aqlm_status_string", "aqlm_abi_version")
 ABI_VERSION = 1
 SCHEMES = {(2, 8, 8): "2x8", (1, 16, 8): "1x16", (1, 16, 16): "1x16g16"}
 
@@ -71,6 +71,10 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [lp, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.aqlm_gemv_batched.argtypes = [lp, ctypes.POINTER(ctypes.c_void_p),
+                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
+                                      ctypes.c_int64, ctypes.c_void_p]
+    lib.aqlm_gemv_batched.restype = ctypes.c_int
     lib.aqlm_status_string.argtypes = [ctypes.c_int]
     lib.aqlm_status_string.restype = ctypes.c_char_p
     lib.aqlm_abi_version.argtypes = []
@@ -181,6 +185,42 @@ class AqlmLayer:
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         """Pick the lookup path for <= 8 rows and the matrix-core path above."""
         return self.gemv(x) if x.shape[0] <= 8 else self.gemm(x)
+
+
+def gemv_batched(layers, xs, outs=None):
+    """y_i = x_i . W_i^T for several layers in one call (aqlm_gemv_batched).
+
+    layers: sequence of AqlmLayer; xs: sequence of [batch, in_i] float16 tensors
+    (one per layer, all with the same batch, may repeat); outs: optional
+    preallocated [batch, out_i] tensors. Returns the list of outputs.
+    """
+    lib = load_library()
+    n = len(layers)
+    if len(xs) != n or (outs is not None and len(outs) != n):
+        raise ValueError("one x (and one out) per layer")
+    if n == 0:
+        return []
+    batch = xs[0].shape[0]
+    device = layers[0].device
+    ys = []
+    for i, (L, x) in enumerate(zip(layers, xs)):
+        x = L._check_x(x)
+        if x.shape[0] != batch or L.device != device:
+            raise ValueError("all layers share the batch size and the device")
+        if outs is None:
+            ys.append(torch.empty((batch, L.out_features), dtype=torch.float16, device=device))
+        else:
+            o = outs[i]
+            if (o.shape != (batch, L.out_features) or o.dtype != torch.float16
+                    or not o.is_contiguous() or o.device != device):
+                raise ValueError("out tensors must be contiguous float16 [batch, out] on the device")
+            ys.append(o)
+    structs = (AqlmLayerStruct * n)(*[L._struct for L in layers])
+    xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    with torch.cuda.device(device):
+        _check(lib.aqlm_gemv_batched(structs, xp, yp, n, batch, _stream_handle(device)))
+    return ys
 
 
 def raw_call(fn_name: str, struct: AqlmLayerStruct, *args) -> int:

@@ -2,6 +2,8 @@
 // caller's stream. Nothing here allocates or synchronises.
 #include <limits.h>
 
+#include <vector>
+
 #include "../../include/aqlm.h"
 #include "aqlm_internal.hpp"
 
@@ -82,6 +84,23 @@ int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_
   if (!x || !y) return AQLM_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return AQLM_ERR_ALIGN;
   return from_hip(aqlm::launch_gemv(d, x, (int)batch, y, static_cast<hipStream_t>(stream)));
+}
+
+int aqlm_gemv_batched(const aqlm_layer *layers, const uint16_t *const *x, uint16_t *const *y,
+                      int32_t num_layers, int64_t batch, void *stream) {
+  if (num_layers < 0 || num_layers > 4096) return AQLM_ERR_SHAPE;
+  if (batch < 0 || batch > 8) return AQLM_ERR_BATCH;
+  if (num_layers == 0 || batch == 0) return AQLM_OK;
+  if (!layers || !x || !y) return AQLM_ERR_NULL;
+  std::vector<aqlm::LayerDesc> d(num_layers);
+  for (int i = 0; i < num_layers; ++i) {
+    const int st = check_layer(&layers[i], &d[i]);
+    if (st != AQLM_OK) return st;
+    if (!x[i] || !y[i]) return AQLM_ERR_NULL;
+    if (!aligned16(x[i]) || !aligned16(y[i])) return AQLM_ERR_ALIGN;
+  }
+  return from_hip(aqlm::launch_gemv_batched(d.data(), x, y, num_layers, (int)batch,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,

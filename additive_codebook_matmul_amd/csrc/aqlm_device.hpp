@@ -25,6 +25,36 @@ __device__ __forceinline__ void store_nt16(void *p, const uint4 &w) {
   __builtin_nontemporal_store(v, static_cast<u32x4_t *>(p));
 }
 
+// Raw buffer resources (gfx9 descriptor word 3 = 0x00020000): loads at
+// offsets outside [0, num_records) return zero instead of faulting, which lets
+// bounds-checked loads stay branch-free.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// streaming variant (non-temporal: data read once)
+__device__ __forceinline__ uint4 buf_load16_nt(Rsrc r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// 16-bit load zero-extended into its own 32-bit register (kept unpacked so a
+// refill never has to merge into a register another value lives in).
+__device__ __forceinline__ uint32_t buf_load_u16(Rsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+// fp16 bits in the low half of a register -> float, without masking the
+// register first (the conversion reads only bits 0..15).
+__device__ __forceinline__ float low_half_to_float(uint32_t reg) {
+  float f;
+  asm("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"(reg));
+  return f;
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
@@ -101,6 +131,19 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, BANK_MASK,
                                          BOUND_CTRL));
+}
+
+// Sum over aligned groups of LPR lanes (16, 32 or 64) in a fixed order; the
+// group's total is valid in its last lane.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  if constexpr (LPR >= 32) v += dpp<kDppRowBcast15, 0xA>(v);
+  if constexpr (LPR >= 64) v += dpp<kDppRowBcast31, 0xC>(v);
+  return v;
 }
 
 // Sum over the 64 lanes of a wavefront in a fixed order; the total is valid in

@@ -33,5 +33,7 @@ hipError_t launch_gemv(const LayerDesc &L, const uint16_t *x, int batch, uint16_
                        hipStream_t stream);
 hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                        hipStream_t stream);
+hipError_t launch_gemv_batched(const LayerDesc *Ls, const uint16_t *const *xs,
+                               uint16_t *const *ys, int n, int batch, hipStream_t stream);
 
 }  // namespace aqlm

@@ -1,18 +1,21 @@
 """Benchmark: batch-1 AQLM GEMV over the Llama-2-7B linear-layer set (scheme 2x8).
 
-One step = aqlm_gemv on each of the seven Llama-2-7B linear layers
+One step = the seven Llama-2-7B linear layers of one transformer block
 (q, k, v, o: 4096x4096; gate, up: 11008x4096; down: 4096x11008), scheme 2x8
-(two 8-bit codebooks, codeword length 8), one activation row, on seeded
-synthetic weights. The codes, scales, activations and outputs are rotated
-over enough distinct copies (>= 1 GiB of codes) that every step reads its
-codes from HBM, not from the 256 MiB last-level cache; the 8 KiB codebooks
-are shared.
+(two 8-bit codebooks, codeword length 8), one activation row, seeded
+synthetic weights, issued the way a decode step can issue them: q, k and v
+share their input and go out as one aqlm_gemv_batched call, then o, then gate
+and up (shared input) as one batched call, then down. The codes, scales,
+activations and outputs are rotated over enough distinct copies (>= 1 GiB of
+codes) that every step reads its codes from HBM, not from the 256 MiB
+last-level cache; the 8 KiB codebooks are shared.
 
 Reported value: achieved HBM GB/s = (codes + x + y bytes of the seven layers)
 / time per step, timed with HIP events on the stream the kernels run on,
-bracketed by device synchronisation. Also reported: microseconds per layer,
-the roofline object of the GEMV kernel and the CPU oracle timed on a bounded
-sample of the same workload.
+bracketed by device synchronisation. Also reported: microseconds per layer
+launched alone, the whole block as a single batched call, the roofline
+object of the dominant kernel (the grouped GEMV of the q|k|v and gate|up
+calls) and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -33,7 +36,7 @@ METRIC = "AQLM GEMV µs/layer + achieved HBM GB/s (% of peak), Llama-2-7B shapes
 WORKLOAD = "llama2_7b_2x8"
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
-GEMV_KERNEL = "gemv_fast_kernel<2x8, batch 1>"
+GEMV_KERNEL = "gemv_2x8_group_kernel (grouped 2x8 GEMV, batch 1, one code chunk per lane)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_2x8_llama2_7b_b1_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "additive_codebook_matmul_amd", "csrc", "gemv.hip")
 
@@ -108,7 +111,7 @@ def main():
     import numpy as np
     import torch
 
-    from additive_codebook_matmul_amd import AqlmLayer, load_library
+    from additive_codebook_matmul_amd import AqlmLayer, gemv_batched, load_library
     from additive_codebook_matmul_amd import workloads as WL
 
     load_library()
@@ -129,65 +132,139 @@ def main():
     for (layer, d, x, _) in layers_np:
         base.append((torch.from_numpy(d.codes).to(dev), torch.from_numpy(d.codebooks).to(dev),
                      torch.from_numpy(d.scales).to(dev), torch.from_numpy(x).to(dev)))
+    names = [l.name for (l, _, _, _) in layers_np]
+    idx = {n: i for i, n in enumerate(names)}
     rot = []
     for c in range(copies):
         row = []
         for (codes, books, scales, x) in base:
             L = AqlmLayer(codes.clone(), books, scales.clone())
-            xx = x.clone()
             yy = torch.empty((1, L.out_features), dtype=torch.float16, device=dev)
-            row.append((L, xx, yy))
+            row.append((L, x.clone(), yy))
+        # q, k, v share one input, as do gate and up
+        row[idx["k"]] = (row[idx["k"]][0], row[idx["q"]][1], row[idx["k"]][2])
+        row[idx["v"]] = (row[idx["v"]][0], row[idx["q"]][1], row[idx["v"]][2])
+        row[idx["up"]] = (row[idx["up"]][0], row[idx["gate"]][1], row[idx["up"]][2])
         rot.append(row)
     torch.cuda.synchronize()
 
-    def step(i):
-        for (L, xx, yy) in rot[i % copies]:
-            L.gemv(xx, out=yy)
+    calls = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
+    call_bytes = {cn: sum(layers_np[idx[n]][3] for n in members) for cn, members in calls}
+    for cn, members in calls:  # shared inputs are read once per call
+        if len(members) > 1:
+            call_bytes[cn] -= (len(members) - 1) * 2 * layers_np[idx[members[0]]][0].in_features
 
+    def issue(i, cn, members):
+        row = rot[i % copies]
+        if len(members) == 1:
+            L, xx, yy = row[idx[members[0]]]
+            L.gemv(xx, out=yy)
+        else:
+            items = [row[idx[m]] for m in members]
+            gemv_batched([it[0] for it in items], [it[1] for it in items],
+                         [it[2] for it in items])
+
+    def step(i):
+        for cn, members in calls:
+            issue(i, cn, members)
+
+    def capture(fn):
+        """A HIP graph of fn's launches (outputs are preallocated: nothing allocates)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, reps):
+        """Mean milliseconds per replay, HIP events on the replay stream."""
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    # one graph holds one step on each rotated copy; a replay is `copies` steps
+    step_graph = capture(lambda: [step(i) for i in range(copies)])
+    for _ in range(max(1, args.warmup // copies)):
+        step_graph.replay()
+    reps = max(1, -(-args.steps // copies))
+    torch.cuda.synchronize()
+    ms_per_step = time_graph(step_graph, reps) / copies
+    steps_timed = reps * copies
+
+    # eager issue of the same step (host launch overhead included), for context
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
     for i in range(args.steps):
-        step(args.warmup + i)
-    end.record()
+        step(i)
+    t1.record()
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
+    eager_ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # per-layer timing: the same layer launched back to back over the rotated copies
+    # per call and per layer: graphs of back-to-back launches over the copies
+    call_us = {}
+    for cn, members in calls:
+        g = capture(lambda cn=cn, members=members: [issue(i, cn, members) for i in range(copies)])
+        call_us[cn] = 1e3 * time_graph(g, max(1, args.layer_iters // copies)) / copies
     us_layer, gbps_layer = {}, {}
     for li, (layer, _, _, nbytes) in enumerate(layers_np):
-        for i in range(10):
-            L, xx, yy = rot[i % copies][li]
-            L.gemv(xx, out=yy)
-        torch.cuda.synchronize()
-        start.record()
-        for i in range(args.layer_iters):
-            L, xx, yy = rot[i % copies][li]
-            L.gemv(xx, out=yy)
-        end.record()
-        torch.cuda.synchronize()
-        us = start.elapsed_time(end) * 1e3 / args.layer_iters
+        def one_layer(li=li):
+            for i in range(copies):
+                L, xx, yy = rot[i][li]
+                L.gemv(xx, out=yy)
+        g = capture(one_layer)
+        us = 1e3 * time_graph(g, max(1, args.layer_iters // copies)) / copies
         us_layer[layer.name] = round(us, 3)
         gbps_layer[layer.name] = round(nbytes / us / 1e3, 1)
 
-    step_bytes = sum(nb for (_, _, _, nb) in layers_np)
+    # the whole block as one batched call (independent inputs)
+    def one_call_all():
+        for i in range(copies):
+            row = rot[i]
+            gemv_batched([r[0] for r in row], [r[1] for r in row], [r[2] for r in row])
+    g = capture(one_call_all)
+    one_call_us = 1e3 * time_graph(g, max(1, args.layer_iters // copies)) / copies
+
+    # dominant kernel: the grouped GEMV of the q|k|v and gate|up calls, launched
+    # back to back (one launch per call) inside the timed graph
+    def dominant():
+        for i in range(copies):
+            issue(i, "qkv", ["q", "k", "v"])
+            issue(i, "gate_up", ["gate", "up"])
+    g = capture(dominant)
+    dom_ms = time_graph(g, max(1, args.layer_iters // copies))
+    dom_launches = 2 * copies
+
+    step_bytes = sum(call_bytes.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    launches = len(layers_np)
+    dom_bytes = call_bytes["qkv"] + call_bytes["gate_up"]
+    dom_avg_us = 1e3 * dom_ms / dom_launches
+    achieved = (dom_bytes / 2) / (dom_avg_us * 1e-6) / 1e9
     traffic = _traffic()
     roofline = {
         "bound": "hbm",
         "kernel": GEMV_KERNEL,
-        "achieved": round(value, 1),
+        "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
-        "frac": round(value / HBM_PEAK_GBPS, 4),
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
-        "bytes_per_launch_avg": step_bytes // launches,
-        "avg_launch_us": round(ms_per_step * 1e3 / launches, 3),
+        "bytes_per_launch_avg": dom_bytes // 2,
+        "avg_launch_us": round(dom_avg_us, 3),
     }
 
     result = {
@@ -195,7 +272,7 @@ def main():
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps_timed,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
@@ -210,11 +287,17 @@ def main():
             "layers": {l.name: [l.out_features, l.in_features] for (l, _, _, _) in layers_np},
             "bytes_per_step": step_bytes,
             "rotated_copies": copies,
+            "step_calls": {cn: members for cn, members in calls},
+            "us_per_call": {k: round(v, 3) for k, v in call_us.items()},
             "us_per_layer": us_layer,
             "gbps_per_layer": gbps_layer,
             "pct_of_peak_per_layer": {k: round(100 * v / HBM_PEAK_GBPS, 1)
                                       for k, v in gbps_layer.items()},
             "accumulate": "fp32",
+            "issue": "HIP graph of the step's launches (eager issue in eager_ms_per_step)",
+            "eager_ms_per_step": round(eager_ms_per_step, 5),
+            "block_as_one_call_us": round(one_call_us, 3),
+            "block_as_one_call_gbps": round(sum(nb for (_, _, _, nb) in layers_np) / one_call_us / 1e3, 1),
         },
         "roofline": roofline,
     }

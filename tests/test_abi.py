@@ -119,3 +119,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         _lib.load_library()
+
+
+def test_batched_validation():
+    lib = _lib.load_library()
+    n = 2
+    structs = (_lib.AqlmLayerStruct * n)(_layer(), _layer(M=3))
+    xs = (ctypes.c_void_p * n)(FAKE, FAKE)
+    ys = (ctypes.c_void_p * n)(FAKE, FAKE + 0x1000)
+    f = lib.aqlm_gemv_batched
+    assert f(structs, xs, ys, -1, 1, None) == 2
+    assert f(structs, xs, ys, 5000, 1, None) == 2
+    assert f(structs, xs, ys, n, 9, None) == 5
+    assert f(structs, xs, ys, n, -1, None) == 5
+    assert f(None, xs, ys, n, 1, None) == 1
+    assert f(structs, None, ys, n, 1, None) == 1
+    # the second layer has an unsupported scheme: nothing launches
+    assert f(structs, xs, ys, n, 1, None) == 3
+    good = (_lib.AqlmLayerStruct * n)(_layer(), _layer())
+    bad_y = (ctypes.c_void_p * n)(FAKE, MISALIGNED)
+    assert f(good, xs, bad_y, n, 1, None) == 4
+    null_x = (ctypes.c_void_p * n)(FAKE, 0)
+    assert f(good, null_x, ys, n, 1, None) == 1
+    # no-ops launch nothing
+    assert f(good, xs, ys, 0, 1, None) == 0
+    assert f(good, xs, ys, n, 0, None) == 0
