@@ -14,7 +14,7 @@ Reported value: achieved HBM GB/s = (codes + x + y bytes of the seven layers)
 / time per step, timed with HIP events on the stream the kernels run on,
 bracketed by device synchronisation. Also reported: microseconds per layer
 launched alone, the whole block as a single batched call, the roofline
-object of the dominant kernel (the grouped GEMV of the q|k|v and gate|up
+object of the dominant kernel (the grouped GEMV of the q,k,v and gate,up
 calls) and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -49,7 +49,26 @@ def _parse():
     p.add_argument("--layer-iters", type=int, default=200,
                    help="launches per layer for the per-layer timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--workload", default=WORKLOAD,
+                   help="llama2_7b_2x8 (default: the headline step), or per-layer tables for "
+                        "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, dequant")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run device-to-device copies of MIB MiB (for scaling the HBM "
+                        "byte counters of a profiler) and exit")
     return p.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """Plain copies of a known size: the reference for FETCH_SIZE / WRITE_SIZE readings."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
 
 
 def _source_hash() -> str:
@@ -66,7 +85,7 @@ def _traffic():
         return None
     if t.get("kernel_source_sha256_16") != _source_hash():
         return None
-    return t.get("bytes_per_step")
+    return t.get("bytes_per_launch")
 
 
 def cpu_baseline(layers_np, budget_s: float = 12.0):
@@ -101,8 +120,96 @@ def cpu_baseline(layers_np, budget_s: float = 12.0):
     }
 
 
+def _capture(torch, fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_graph(torch, g, reps):
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def per_layer_tables(args):
+    """Per-layer launch times for the other workloads (one JSON line each).
+
+    Every layer is launched back to back over rotated copies of its codes
+    (>= 1 GiB) inside a HIP graph; the time per launch is the graph's time over
+    the launch count. GEMV and dequant rows report HBM GB/s (codes + x + y, or
+    codes + W written); GEMM rows also report fp16 matrix-core TFLOP/s.
+    """
+    import torch
+    from additive_codebook_matmul_amd import AqlmLayer, load_library
+    from additive_codebook_matmul_amd import workloads as WL
+    load_library()
+    dev = torch.device("cuda:0")
+    name = args.workload
+    wl = WL.WORKLOADS["llama2_7b_2x8" if name == "dequant" else name]
+    rows = []
+    for layer in wl.layers:
+        d = WL.make_layer(layer)
+        codes = torch.from_numpy(d.codes.view("int16") if d.codes.dtype.name == "uint16" else d.codes).to(dev)
+        books = torch.from_numpy(d.codebooks).to(dev)
+        scales = torch.from_numpy(d.scales).to(dev)
+        batches = (1,) if name == "dequant" else wl.batches
+        for batch in batches:
+            b = WL.workload_bytes(layer, batch)
+            copies = max(2, min(64, -(-ROTATE_BYTES // b["codes"])))
+            if name == "gemm_mlp":
+                copies = max(2, min(copies, 8))
+            Ls = [AqlmLayer(codes.clone(), books, scales) for _ in range(copies)]
+            x = torch.from_numpy(WL.make_x(layer, batch)).to(dev)
+            if name == "dequant":
+                w = torch.empty((layer.out_features, layer.in_features), dtype=torch.float16, device=dev)
+                fn = lambda: [L.dequant(out=w) for L in Ls]
+                nbytes = b["codes"] + 2 * layer.out_features * layer.in_features
+            else:
+                y = torch.empty((batch, layer.out_features), dtype=torch.float16, device=dev)
+                op = "gemm" if name == "gemm_mlp" else "gemv"
+                fn = lambda op=op: [getattr(L, op)(x, out=y) for L in Ls]
+                nbytes = b["codes"] + b["x"] + b["y"]
+            g = _capture(torch, fn)
+            reps = max(2, 200 // copies)
+            us = 1e3 * _time_graph(torch, g, reps) / copies
+            row = {"layer": layer.name, "out": layer.out_features, "in": layer.in_features,
+                   "scheme": layer.scheme.name, "batch": batch, "us": round(us, 3),
+                   "hbm_gbps": round(nbytes / us / 1e3, 1),
+                   "pct_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBPS, 2)}
+            if name == "gemm_mlp":
+                flops = 2 * batch * layer.out_features * layer.in_features
+                row["tflops"] = round(flops / us / 1e6, 2)
+                row["pct_fp16_mfma_peak"] = round(100 * flops / us / 1e6 / 2500.0, 2)
+            rows.append(row)
+            print(json.dumps({"workload": name, **row}), flush=True)
+            del Ls, g
+            torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = _parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.workload != WORKLOAD:
+        per_layer_tables(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path runs on a single MI355X)", file=sys.stderr)
@@ -239,7 +346,7 @@ def main():
     g = capture(one_call_all)
     one_call_us = 1e3 * time_graph(g, max(1, args.layer_iters // copies)) / copies
 
-    # dominant kernel: the grouped GEMV of the q|k|v and gate|up calls, launched
+    # dominant kernel: the grouped GEMV of the q,k,v and gate,up calls, launched
     # back to back (one launch per call) inside the timed graph
     def dominant():
         for i in range(copies):
