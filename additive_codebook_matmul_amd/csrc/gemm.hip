@@ -17,6 +17,9 @@
 // The MFMA K index of every lane element is paired identically in A and B, so
 // any assignment of groups to MFMA steps gives the same sum; for g = 8 the two
 // lane halves take groups s and s + 4 of the K block in step s.
+#include <atomic>
+#include <type_traits>
+
 #include "aqlm_device.hpp"
 
 namespace aqlm {
@@ -209,9 +212,343 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny tiles for few activation rows: v_mfma_f32_16x16x32_f16 on 16 output
+// rows x 16 activation rows. Lane l feeds row (A) or activation row (B)
+// l % 16 and K slice l / 16 of eight inputs; it holds output rows
+// 4 * (l / 16) .. + 3 of activation row l % 16 in its accumulator.
+//
+// A block owns 16 output rows and NT tiles of 16 activation rows; its waves
+// split the input dimension into contiguous ranges of chunks, and their
+// float32 partial sums are added in LDS in wave order (deterministic). A chunk
+// is one 16-byte code load per lane (8 groups): 32 groups (256 inputs) for
+// g = 8, 16 groups for g = 16, consumed in 8 MFMA steps.
+//
+// K order: in step s, lane quarter q takes the 16-byte column block 4s + q of
+// the chunk's 512 activation bytes: group 4s + q (g = 8), or half q % 2 of
+// group 2s + q / 2 (g = 16). A and B use the same map, so the MFMA's K order
+// is a permutation of the inputs and the sum is unchanged. A lane loads 8
+// consecutive codes of its row; a per-wave LDS transpose puts them in step
+// order.
+//
+// Activations: the B layout gives the four 16-byte pieces of one activation
+// row to lanes l, l + 16, l + 32, l + 48, so loading fragments directly would
+// never coalesce (the L1 then serves one lane per clock). Each wave instead
+// loads its chunk's activations with fully coalesced 16-byte loads into
+// registers, writes them to a private LDS slot (column block XOR activation
+// row, so fragment reads are free of bank conflicts) and reads its B fragments
+// from there. Codes are loaded kSkinnyCodeDepth chunks ahead, activations (and
+// 1x16 codewords) one chunk ahead.
+constexpr int kSkinnyMaxWaves = 8;
+constexpr int kSkinnyCodeDepth = 4;  // the step loop below is unrolled to match
+constexpr int64_t kSkinnyMaxBatch = 128;  // above this the wide tiles take over
+constexpr int kSkinnyXSlotBytes = 16 * 512;  // one 16-row activation tile of a chunk
+
+// Dynamic LDS of one block: [2x8 codebooks 8 KiB][code transpose 1 KiB per
+// wave][activation slots NT x 8 KiB per wave]; the final reduction reuses the
+// activation slots.
+constexpr int skinny_lds_bytes(bool lut, int nt, int waves) {
+  return (lut ? 8192 : 0) + waves * 1024 + waves * nt * kSkinnyXSlotBytes;
+}
+
+template <Scheme S, int NT, bool ALIGNED>
+__global__ __launch_bounds__(64 * kSkinnyMaxWaves) void gemm_skinny_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
+    uint16_t *__restrict__ y, int out, int in, int groups, int batch, uint32_t codes_bytes,
+    uint32_t x_bytes) {
+  constexpr int G = group_size(S);
+  constexpr int GPC = G == 8 ? 32 : 16;  // groups per chunk
+  constexpr bool LUT = S == Scheme::k2x8;
+  constexpr int CD = kSkinnyCodeDepth;
+  // steps between transposing a chunk's codes and computing it: the 1x16
+  // codeword gathers need them a step earlier
+  constexpr int SA = LUT ? 1 : 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int lane = threadIdx.x & 63, waves = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int r = lane & 15, q = lane >> 4;
+  const int row0 = blockIdx.x * 16, tok0 = blockIdx.y * (16 * NT);
+  const uint32_t row_bytes = (uint32_t)groups * 2u;
+  const int piece = G == 8 ? q : (q >> 1);  // which 8 codes of the chunk the lane loads
+  const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
+
+  uint4 *lds_books = reinterpret_cast<uint4 *>(lds);
+  uint8_t *lds_codes = lds + (LUT ? 8192 : 0);
+  uint8_t *lds_xall = lds_codes + waves * 1024;
+  uint4 *xslot = reinterpret_cast<uint4 *>(lds_xall + wave * NT * kSkinnyXSlotBytes);
+  uint16_t *cslot = reinterpret_cast<uint16_t *>(lds_codes + wave * 1024) + r * 32;
+
+  // Rows >= out and activation rows >= batch start past the end of their
+  // buffers, so their loads return zero.
+  const Rsrc crs = make_rsrc(codes, codes_bytes);
+  const Rsrc xrs = make_rsrc(x, x_bytes);
+  const uint32_t crow = (uint32_t)(row0 + r) * row_bytes;
+  // coalesced activation loads: load j of tile t brings activation rows
+  // 2j + lane / 32 of the tile, 16-byte column block lane % 32
+  const int xl_row = lane >> 5, xl_blk = lane & 31;
+  uint32_t xl_off[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    xl_off[t] = (uint32_t)(tok0 + 16 * t + xl_row) * (uint32_t)in * 2u + (uint32_t)xl_blk * 16u;
+  const uint32_t x_pair_stride = 2u * (uint32_t)in * 2u;  // two activation rows
+
+  const int nchunks = (groups + GPC - 1) / GPC;
+  const int nfull = groups / GPC;
+  const int cb = wave * nchunks / waves, ce = (wave + 1) * nchunks / waves;
+  // full chunks run in the pipelined loop; a partial last chunk runs after it
+  const int nmain = max(0, min(ce, nfull) - cb);
+  // Chunk of step i; steps past the loop repeat its last chunk (a cache hit),
+  // so prefetching never streams extra code bytes.
+  auto chunk_of = [&](int i) { return cb + min(i, nmain - 1); };
+
+  auto load_codes = [&](int c, uint32_t (&cw)[4]) {
+    const uint32_t off = crow + (uint32_t)(c * GPC + piece * 8) * 2u;
+    if constexpr (ALIGNED) {
+      const uint4 v = buf_load16(crs, off);
+      cw[0] = v.x;
+      cw[1] = v.y;
+      cw[2] = v.z;
+      cw[3] = v.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        cw[i] = buf_load_u16(crs, off + 4u * i) | (buf_load_u16(crs, off + 4u * i + 2u) << 16);
+    }
+  };
+  auto load_x = [&](int c, uint4 (&xr)[NT][8]) {
+    const uint32_t cbyte = (uint32_t)c * 512u;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xr[t][j] = buf_load16(xrs, xl_off[t] + j * x_pair_stride + cbyte);
+  };
+  auto store_x = [&](const uint4 (&xr)[NT][8]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 2 * j + xl_row;
+        xslot[t * 512 + row * 32 + (xl_blk ^ row)] = xr[t][j];
+      }
+  };
+  auto frag = [&](int t, int s) { return xslot[t * 512 + r * 32 + ((4 * s + q) ^ r)]; };
+
+  // Transpose the row's chunk codes through this wave's LDS slot so that
+  // sc holds the lane's codes in step order (two per register).
+  auto stage = [&](const uint32_t (&cw)[4], uint32_t (&sc)[4]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = piece * 8 + i;  // code index within the chunk row
+      const int pos = G == 8 ? (k & 3) * 8 + (k >> 2) : (k & 1) * 8 + (k >> 1);
+      cslot[pos] = (uint16_t)(cw[i >> 1] >> ((i & 1) * 16));
+    }
+    const uint4 v = *reinterpret_cast<const uint4 *>(cslot + (G == 8 ? q : (q >> 1)) * 8);
+    sc[0] = v.x;
+    sc[1] = v.y;
+    sc[2] = v.z;
+    sc[3] = v.w;
+  };
+  auto code_of = [](const uint32_t (&sc)[4], int s) {
+    return (sc[s >> 1] >> ((s & 1) * 16)) & 0xFFFFu;
+  };
+  auto gather = [&](const uint32_t (&sc)[4], uint4 (&ga)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t code = code_of(sc, s);
+      ga[s] = gbooks[G == 8 ? code : 2u * code + (uint32_t)(q & 1)];
+    }
+  };
+
+  float4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Four MFMA steps at a time: every LDS read of the four is issued before
+  // the first add, so their latencies overlap instead of adding up.
+  auto compute = [&](auto masked, int c, const uint32_t (&sc)[4], const uint4 (&ga)[8]) {
+    constexpr bool MASK = decltype(masked)::value;
+#pragma unroll
+    for (int h = 0; h < 8; h += 4) {
+      uint4 c0[4], c1[4], b[4][NT];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = h + u;
+        if constexpr (LUT) {
+          const uint32_t code = code_of(sc, s);
+          c0[u] = lds_books[code & 0xFFu];
+          c1[u] = lds_books[256u + (code >> 8)];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) b[u][t] = frag(t, s);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = h + u;
+        uint4 a = LUT ? hadd8(c0[u], c1[u]) : ga[s];
+        if constexpr (MASK) {
+          // 16-byte column blocks past the end of the row: zero both operands
+          if (c * 512 + (4 * s + q) * 16 >= in * 2) {
+            a = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) b[u][t] = make_uint4(0, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                         __builtin_bit_cast(half8_t, b[u][t]),
+                                                         acc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  // Register rings indexed statically (the step loop is unrolled CD times):
+  // moving a register whose load is still in flight would stall on it.
+  uint32_t cw[CD][4];  // raw codes, CD chunks ahead
+  uint32_t sc[4][4];   // codes in step order
+  uint4 xr[NT][8];     // next chunk's activations on their way to LDS
+  uint4 ga[2][8];      // 1x16 codewords (unused by the LDS lookup)
+  if (nmain > 0) {
+    load_x(chunk_of(0), xr);
+#pragma unroll
+    for (int i = 0; i < CD; ++i) load_codes(chunk_of(i), cw[i]);
+  }
+  if constexpr (LUT) {
+    // issued after the first chunk's loads so that the latencies overlap
+    for (int i = threadIdx.x; i < 512; i += blockDim.x) lds_books[i] = gbooks[i];
+    __syncthreads();
+  }
+  if (nmain > 0) {
+    store_x(xr);
+#pragma unroll
+    for (int i = 0; i < SA; ++i) stage(cw[i], sc[i]);
+    if constexpr (!LUT) gather(sc[0], ga[0]);
+  }
+
+  // Step i (code slot K = i % CD). Loads are issued in the order activations,
+  // codewords, codes, so that waiting for the first two never waits for the
+  // codes fetched CD steps ahead (vmcnt retires in order).
+  auto step = [&](int i, auto kc) {
+    constexpr int K = decltype(kc)::value;
+    load_x(chunk_of(i + 1), xr);
+    stage(cw[(K + SA) % CD], sc[(K + SA) & 3]);
+    if constexpr (!LUT) gather(sc[(K + 1) & 3], ga[(K + 1) & 1]);
+    load_codes(chunk_of(i + CD), cw[K]);
+    compute(std::false_type{}, chunk_of(i), sc[K], ga[K & 1]);
+    // overwrites this chunk's activations: the fragment reads above are
+    // ahead of these writes in the wave's LDS queue
+    store_x(xr);
+  };
+  int i = 0;
+  for (; i + CD <= nmain; i += CD) {
+    step(i, std::integral_constant<int, 0>{});
+    step(i + 1, std::integral_constant<int, 1>{});
+    step(i + 2, std::integral_constant<int, 2>{});
+    step(i + 3, std::integral_constant<int, 3>{});
+  }
+  if (i < nmain) step(i, std::integral_constant<int, 0>{});
+  if (i + 1 < nmain) step(i + 1, std::integral_constant<int, 1>{});
+  if (i + 2 < nmain) step(i + 2, std::integral_constant<int, 2>{});
+
+  if (ce > nfull) {
+    // the partial last chunk (only the last wave has one), unpipelined
+    const int c = nfull;
+    uint32_t tcw[4], tsc[4];
+    load_codes(c, tcw);
+    load_x(c, xr);
+    stage(tcw, tsc);
+    if constexpr (!LUT) gather(tsc, ga[0]);
+    store_x(xr);
+    compute(std::true_type{}, c, tsc, ga[0]);
+  }
+
+  // Epilogue: add the waves' partial sums in wave order, scale, round.
+  auto write = [&](int t, int l, const float4_t &v) {
+    const int tok = tok0 + 16 * t + (l & 15);
+    if (tok >= batch) return;
+    const int rb = row0 + 4 * (l >> 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = rb + k;
+      if (row < out) y[(int64_t)tok * out + row] = (uint16_t)f2h(v[k] * h2f(scales[row]));
+    }
+  };
+  if (waves == 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) write(t, lane, acc[t]);
+    return;
+  }
+  float4_t *red = reinterpret_cast<float4_t *>(lds_xall);
+  __syncthreads();  // every wave is done with its activation slot
+#pragma unroll
+  for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  for (int e = threadIdx.x; e < NT * 64; e += blockDim.x) {
+    const int t = e >> 6, l = e & 63;
+    float4_t v = red[t * 64 + l];
+    for (int w = 1; w < waves; ++w) v += red[(w * NT + t) * 64 + l];
+    write(t, l, v);
+  }
+}
+
+template <Scheme S, int NT>
+hipError_t launch_skinny(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
+                         hipStream_t stream) {
+  const int out = (int)L.out, in = (int)L.in, groups = (int)L.groups;
+  constexpr bool LUT = S == Scheme::k2x8;
+  constexpr int GPC = group_size(S) == 8 ? 32 : 16;
+  const int nchunks = (groups + GPC - 1) / GPC;
+  const int row_tiles = (out + 15) / 16;
+  const int tok_blocks = (int)((batch + 16 * NT - 1) / (16 * NT));
+  // enough wavefronts to cover the chip about eight times, at least one chunk each
+  const int64_t wgs = (int64_t)row_tiles * tok_blocks;
+  int waves = 1;
+  while (waves < kSkinnyMaxWaves && wgs * waves < 2048 && waves * 2 <= nchunks) waves *= 2;
+  const dim3 grid(row_tiles, tok_blocks);
+  const uint32_t codes_bytes = (uint32_t)(L.out * L.groups * kCodeBytesPerGroup);
+  const uint32_t x_bytes = (uint32_t)(batch * L.in * 2);
+  const uint8_t *codes = static_cast<const uint8_t *>(L.codes);
+  const size_t lds = skinny_lds_bytes(LUT, NT, waves);
+  const bool aligned = groups % 8 == 0;
+  auto k = aligned ? gemm_skinny_kernel<S, NT, true> : gemm_skinny_kernel<S, NT, false>;
+  static_assert(skinny_lds_bytes(LUT, NT, kSkinnyMaxWaves) <= 160 * 1024, "LDS budget");
+  if (lds > 64 * 1024) {
+    // more than the default dynamic LDS limit: raise it once per device
+    static std::atomic<uint64_t> raised[2]{};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (dev >= 64 || !(raised[aligned].load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              skinny_lds_bytes(LUT, NT, kSkinnyMaxWaves));
+      if (e != hipSuccess) return e;
+      raised[aligned].fetch_or(bit, std::memory_order_acq_rel);
+    }
+  }
+  hipLaunchKernelGGL(k, grid, dim3(64 * waves), lds, stream, codes, L.books, L.scales, x, y, out,
+                     in, groups, (int)batch, codes_bytes, x_bytes);
+  return hipGetLastError();
+}
+
+// Byte offsets of the skinny kernel are 32-bit: rows past the end (up to 15)
+// and chunks read ahead must stay below 2^32.
+bool skinny_fits(const LayerDesc &L, int64_t batch, int nt) {
+  const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
+  const int64_t code_span = (L.out + 16) * row_bytes + 4096;
+  const int64_t x_span = (batch + 16 * nt) * L.in * 2 + 4096;
+  return code_span < (int64_t(1) << 32) && x_span < (int64_t(1) << 32);
+}
+
 template <Scheme S>
 hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                          hipStream_t stream) {
+  if (batch <= 16 && skinny_fits(L, batch, 1)) return launch_skinny<S, 1>(L, x, batch, y, stream);
+  if (batch <= kSkinnyMaxBatch && skinny_fits(L, batch, 2))
+    return launch_skinny<S, 2>(L, x, batch, y, stream);
   const int out = (int)L.out, in = (int)L.in, groups = (int)L.groups;
   const dim3 grid((out + kBM - 1) / kBM, (unsigned)((batch + kBN - 1) / kBN));
   const uint8_t *codes = static_cast<const uint8_t *>(L.codes);

@@ -27,7 +27,8 @@ SCHEMES = {"2x8": WL.S2x8, "1x16": WL.S1x16, "1x16g16": WL.S1x16g16}
 
 # (out, groups): single row/group, ragged rows and groups, multiples of the
 # 16-byte code chunk (8 groups) with and without row tails, several tiles.
-SMALL_SHAPES = [(1, 1), (7, 5), (64, 8), (255, 13), (300, 64), (33, 172), (513, 24), (257, 9)]
+SMALL_SHAPES = [(1, 1), (7, 5), (64, 8), (255, 13), (300, 64), (33, 172), (513, 24), (257, 9),
+                (70, 200)]
 
 
 def _small(scheme, out, J, batch, seed):
@@ -70,7 +71,7 @@ def test_small_gemm(sname, out, J):
     s = SCHEMES[sname]
     codes, books, scales, x = _small(s, out, J, 130, seed=out * 23 + J)
     layer = dev_layer(codes, books, scales)
-    for batch in (1, 5, 64, 65, 130):
+    for batch in (1, 5, 16, 17, 32, 33, 64, 65, 130):
         y = layer.gemm(dev_x(x[:batch]))
         y_ref, bound = oracle.forward(x[:batch], codes, books, scales)
         assert_product(y, y_ref, bound, f"gemm {sname} {out}x{J} b{batch}")
