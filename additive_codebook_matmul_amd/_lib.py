@@ -101,7 +101,7 @@ def _stream_handle(device: torch.device) -> int:
 class AqlmLayer:
     """A quantized linear layer held as device tensors in the packed format.
 
-    codes      [out, in/g, M]  torch.uint8 (B = 8) or torch.int16/uint16 bits (B = 16)
+    codes      [out, in/g, M]  torch.uint8 (B = 8) or torch.int16/uint16 bits (B > 8)
     codebooks  [M, 2**B, g]    torch.float16
     scales     [out]           torch.float16
     """
@@ -116,8 +116,8 @@ class AqlmLayer:
         if ncode < 2 or ncode & (ncode - 1):
             raise ValueError("codebook size must be a power of two")
         B = ncode.bit_length() - 1
-        want = torch.uint8 if B == 8 else (torch.int16, torch.uint16)
-        if (B == 8 and codes.dtype != torch.uint8) or (B == 16 and codes.dtype not in want):
+        want = (torch.uint8,) if B <= 8 else (torch.int16, torch.uint16)
+        if codes.dtype not in want:
             raise ValueError(f"codes dtype {codes.dtype} does not match {B}-bit codes")
         if codebooks.dtype != torch.float16 or scales.dtype != torch.float16:
             raise ValueError("codebooks and scales must be float16")
@@ -139,6 +139,11 @@ class AqlmLayer:
     @property
     def scheme(self) -> str:
         return SCHEMES.get((self.M, self.B, self.g), f"{self.M}x{self.B}g{self.g}")
+
+    @property
+    def general(self) -> bool:
+        """True when the scheme runs the library's general kernels."""
+        return (self.M, self.B, self.g) not in SCHEMES
 
     def _check_x(self, x: torch.Tensor) -> torch.Tensor:
         if x.dim() != 2 or x.shape[1] != self.in_features:

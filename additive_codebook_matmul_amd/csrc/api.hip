@@ -23,6 +23,8 @@ int check_layer(const aqlm_layer *layer, aqlm::LayerDesc *d) {
     s = aqlm::Scheme::k1x16;
   else if (M == 1 && B == 16 && g == 16)
     s = aqlm::Scheme::k1x16g16;
+  else if (M >= 1 && M <= 8 && B >= 8 && B <= 16 && (g == 8 || g == 16))
+    s = aqlm::Scheme::kGeneral;
   else
     return AQLM_ERR_SCHEME;
   if (layer->reserved != 0) return AQLM_ERR_SHAPE;
@@ -36,6 +38,9 @@ int check_layer(const aqlm_layer *layer, aqlm::LayerDesc *d) {
   d->in = layer->in_features;
   d->groups = layer->in_features / g;
   d->scheme = s;
+  d->M = M;
+  d->B = B;
+  d->g = g;
   d->codes = layer->codes;
   d->books = layer->codebooks;
   d->scales = layer->scales;
@@ -56,8 +61,8 @@ const char *aqlm_status_string(int status) {
     case AQLM_ERR_NULL: return "a required pointer is NULL";
     case AQLM_ERR_SHAPE: return "invalid shape: need out >= 1, in >= 1, in % group_size == 0, "
                                 "sizes below 2^30 and reserved == 0";
-    case AQLM_ERR_SCHEME: return "unsupported scheme: (M, B, g) must be (2, 8, 8), (1, 16, 8) "
-                                 "or (1, 16, 16)";
+    case AQLM_ERR_SCHEME: return "unsupported scheme: need 1 <= M <= 8 codebooks, 8 <= B <= 16 "
+                                 "code bits and group size 8 or 16";
     case AQLM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case AQLM_ERR_BATCH: return "batch outside the entry point's range";
     case AQLM_ERR_HIP: return "the HIP runtime reported an error";

@@ -8,9 +8,10 @@ namespace aqlm {
 
 // The three codebook schemes (M codebooks, B-bit codes, codeword length g).
 enum class Scheme : int {
-  k2x8 = 0,     // M = 2, B = 8,  g = 8
-  k1x16 = 1,    // M = 1, B = 16, g = 8
-  k1x16g16 = 2  // M = 1, B = 16, g = 16
+  k2x8 = 0,      // M = 2, B = 8,  g = 8
+  k1x16 = 1,     // M = 1, B = 16, g = 8
+  k1x16g16 = 2,  // M = 1, B = 16, g = 16
+  kGeneral = 3   // any other M = 1..8, B = 8..16, g = 8 or 16
 };
 
 struct LayerDesc {
@@ -18,14 +19,15 @@ struct LayerDesc {
   int64_t in;            // input columns
   int64_t groups;        // in / g
   Scheme scheme;
-  const void *codes;     // [out][groups][M], 2 bytes per group in every scheme
+  int M, B, g;           // codebooks, code bits, codeword length
+  const void *codes;     // [out][groups][M]; uint8 codes when B == 8, uint16 when B > 8
   const uint16_t *books; // [M][2^B][g] fp16 bits
   const uint16_t *scales;// [out] fp16 bits
 };
 
 constexpr int group_size(Scheme s) { return s == Scheme::k1x16g16 ? 16 : 8; }
 
-// Every supported scheme stores exactly two bytes of codes per group.
+// The three dedicated schemes store exactly two bytes of codes per group.
 constexpr int kCodeBytesPerGroup = 2;
 
 hipError_t launch_dequant(const LayerDesc &L, uint16_t *W, hipStream_t stream);
@@ -33,6 +35,12 @@ hipError_t launch_gemv(const LayerDesc &L, const uint16_t *x, int batch, uint16_
                        hipStream_t stream);
 hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                        hipStream_t stream);
+// Kernels for Scheme::kGeneral (general.hip).
+hipError_t launch_dequant_general(const LayerDesc &L, uint16_t *W, hipStream_t stream);
+hipError_t launch_gemv_general(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
+                               hipStream_t stream);
+hipError_t launch_gemm_general(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
+                               hipStream_t stream);
 hipError_t launch_gemv_batched(const LayerDesc *Ls, const uint16_t *const *xs,
                                uint16_t *const *ys, int n, int batch, hipStream_t stream);
 

@@ -96,6 +96,8 @@ hipError_t launch_dequant(const LayerDesc &L, uint16_t *W, hipStream_t stream) {
       hipLaunchKernelGGL(dequant_1x16_kernel<16>, dim3(grid), dim3(kBlock), 0, stream, codes,
                          L.books, L.scales, W, L.groups, total);
       break;
+    case Scheme::kGeneral:
+      return launch_dequant_general(L, W, stream);
   }
   return hipGetLastError();
 }

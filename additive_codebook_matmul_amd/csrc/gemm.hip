@@ -569,6 +569,7 @@ hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uin
     case Scheme::k2x8: return launch_scheme<Scheme::k2x8>(L, x, batch, y, stream);
     case Scheme::k1x16: return launch_scheme<Scheme::k1x16>(L, x, batch, y, stream);
     case Scheme::k1x16g16: return launch_scheme<Scheme::k1x16g16>(L, x, batch, y, stream);
+    case Scheme::kGeneral: return launch_gemm_general(L, x, batch, y, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -539,6 +539,7 @@ hipError_t launch_gemv(const LayerDesc &L, const uint16_t *x, int batch, uint16_
     case Scheme::k2x8: return launch_scheme<Scheme::k2x8>(L, x, batch, y, stream);
     case Scheme::k1x16: return launch_scheme<Scheme::k1x16>(L, x, batch, y, stream);
     case Scheme::k1x16g16: return launch_scheme<Scheme::k1x16g16>(L, x, batch, y, stream);
+    case Scheme::kGeneral: return launch_gemv_general(L, x, batch, y, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -6,7 +6,7 @@ product), so both the HIP path and the CPU oracle can take their inputs
 from it without sharing any computation.
 
 Packed format (one quantized linear layer, out x in):
-  codes      [out, in/g, M]   uint8 (B = 8) or uint16 (B = 16), m fastest
+  codes      [out, in/g, M]   uint8 (B = 8) or uint16 (B > 8), m fastest
   codebooks  [M, 2**B, g]     float16
   scales     [out]            float16
   x          [batch, in]      float16
@@ -20,7 +20,8 @@ codebooks, scales, x, so that the batch size changes only x.
 Shapes follow the linear layers of Llama-2-7B (hidden 4096, MLP 11008) and
 Llama-2-70B (hidden 8192, MLP 28672, grouped-query k/v of 1024 rows); the
 schemes are the pages' "2x8" (two 8-bit codebooks) and "1x16" (one 16-bit
-codebook) with codeword length g = 8, plus a g = 16 variant of 1x16.
+codebook) with codeword length g = 8, plus a g = 16 variant of 1x16, and a
+set of general schemes (1..8 codebooks of 8..16-bit codes, g = 8 or 16).
 """
 from __future__ import annotations
 
@@ -93,6 +94,17 @@ def _gemm_layers(index: int) -> Tuple[Layer, ...]:
     return tuple(out)
 
 
+# Schemes beyond the three named ones: more codebooks, wider codes, both
+# codeword lengths (M x B bits, g), on a Llama-2-7B attention-shaped layer.
+GENERAL_SCHEMES = (Scheme(1, 8, 8), Scheme(3, 8, 8), Scheme(4, 8, 8), Scheme(4, 8, 16),
+                   Scheme(8, 8, 16), Scheme(1, 12, 8), Scheme(2, 12, 16), Scheme(2, 16, 8))
+
+
+def _general_layers(index: int) -> Tuple[Layer, ...]:
+    return tuple(Layer(f"q_{s.name}", 4096, 4096, s, 1000 * index + li)
+                 for li, s in enumerate(GENERAL_SCHEMES))
+
+
 WORKLOADS: Dict[str, Workload] = {
     w.name: w for w in (
         Workload("single_2x8_512x1024", 1,
@@ -107,6 +119,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("gemm_mlp", 5, _gemm_layers(5), (16, 128, 2048),
                  "MLP-shaped layers (11008x4096, 4096x11008), schemes 1x16 g16 "
                  "and 2x8 g8, batch 16/128/2048"),
+        Workload("general_schemes", 6, _general_layers(6), (1, 8, 16),
+                 "4096x4096 layers under general schemes (M = 1..8 codebooks, "
+                 "B = 8..16 bits, g = 8/16), batch 1/8/16"),
     )
 }
 

@@ -51,7 +51,8 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--workload", default=WORKLOAD,
                    help="llama2_7b_2x8 (default: the headline step), or per-layer tables for "
-                        "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, dequant")
+                        "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, "
+                        "general_schemes, dequant")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device-to-device copies of MIB MiB (for scaling the HBM "
                         "byte counters of a profiler) and exit")
@@ -171,17 +172,17 @@ def per_layer_tables(args):
         for batch in batches:
             b = WL.workload_bytes(layer, batch)
             copies = max(2, min(64, -(-ROTATE_BYTES // b["codes"])))
-            if name == "gemm_mlp":
+            if batch > 8:
                 copies = max(2, min(copies, 8))
             Ls = [AqlmLayer(codes.clone(), books, scales) for _ in range(copies)]
             x = torch.from_numpy(WL.make_x(layer, batch)).to(dev)
-            if name == "dequant":
+            op = "dequant" if name == "dequant" else ("gemm" if batch > 8 else "gemv")
+            if op == "dequant":
                 w = torch.empty((layer.out_features, layer.in_features), dtype=torch.float16, device=dev)
                 fn = lambda: [L.dequant(out=w) for L in Ls]
                 nbytes = b["codes"] + 2 * layer.out_features * layer.in_features
             else:
                 y = torch.empty((batch, layer.out_features), dtype=torch.float16, device=dev)
-                op = "gemm" if name == "gemm_mlp" else "gemv"
                 fn = lambda op=op: [getattr(L, op)(x, out=y) for L in Ls]
                 nbytes = b["codes"] + b["x"] + b["y"]
             g = _capture(torch, fn)
@@ -191,7 +192,7 @@ def per_layer_tables(args):
                    "scheme": layer.scheme.name, "batch": batch, "us": round(us, 3),
                    "hbm_gbps": round(nbytes / us / 1e3, 1),
                    "pct_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBPS, 2)}
-            if name == "gemm_mlp":
+            if op == "gemm":
                 flops = 2 * batch * layer.out_features * layer.in_features
                 row["tflops"] = round(flops / us / 1e6, 2)
                 row["pct_fp16_mfma_peak"] = round(100 * flops / us / 1e6 / 2500.0, 2)

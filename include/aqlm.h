@@ -11,7 +11,8 @@
  * / multi-codebook quantization)", field "Bits").
  *
  * Packed format (all arrays dense, row-major, little-endian):
- *   codes      [out][in/g][M]   uint8 when B == 8, uint16 when B == 16; an
+ *   codes      [out][in/g][M]   uint8 when B == 8, uint16 when B > 8 (one
+ *                               code per element, no bit packing); an
  *                               entry is an unsigned codeword index < 2^B
  *   codebooks  [M][2^B][g]      float16 bit patterns
  *   scales     [out]            float16 bit patterns, one per output row
@@ -24,11 +25,15 @@
  * group-to-column map, the scale and the rounding unstated; this is the
  * library's reading of them.
  *
- * Supported schemes (M, B, g): (2, 8, 8) "2x8", (1, 16, 8) "1x16" and
- * (1, 16, 16) "1x16 g16" -- the 8- and 16-dimensional codebook schemes of
+ * Supported schemes: 1 <= M <= 8 codebooks, 8 <= B <= 16 code bits and
+ * codeword length g = 8 or 16 -- the 8- and 16-dimensional codebooks of
  * "Additive quantization that actually survives one-bit weights", sections
- * "Key highlights" and "Caveats". Any in_features that is a multiple of g
- * is accepted.
+ * "Key highlights" and "Caveats", with the number of codebooks and the group
+ * size free as in the ablation of the "Extreme Compression of Large Language
+ * Models via Additive Quantization" summary (table "Measured effects reported
+ * in the paper"). (2, 8, 8) "2x8", (1, 16, 8) "1x16" and (1, 16, 16)
+ * "1x16 g16" run dedicated kernels; every other scheme runs general ones.
+ * Any in_features that is a multiple of g is accepted.
  *
  * Pointers. Every array pointer is a DEVICE pointer on the current HIP
  * device; codes, codebooks, scales, x, y and W must each be 16-byte aligned.
@@ -81,7 +86,7 @@ typedef struct aqlm_layer {
   int32_t nbits;             /* B: codebook size is 2^B */
   int32_t group_size;        /* g: codeword length */
   int32_t reserved;          /* must be 0 */
-  const void *codes;         /* device, [out][in/g][M] uint8 (B=8) / uint16 (B=16) */
+  const void *codes;         /* device, [out][in/g][M] uint8 (B=8) / uint16 (B>8) */
   const uint16_t *codebooks; /* device, [M][2^B][g] float16 bits */
   const uint16_t *scales;    /* device, [out] float16 bits */
 } aqlm_layer;

@@ -20,8 +20,9 @@ What it computes, and where that comes from:
   design notes of the repository):
     - a weight group is g consecutive input columns of one output row:
       group j of row o covers columns j*g .. j*g+g-1, element k <-> column j*g+k;
-    - codes are unsigned indices laid out [out, in/g, M] (m fastest),
-      codebooks [M, 2**B, g], one float16 scale per output row;
+    - codes are unsigned indices laid out [out, in/g, M] (m fastest), one
+      per storage element (uint8 for B = 8, uint16 for 8 < B <= 16, no bit
+      packing), codebooks [M, 2**B, g], one float16 scale per output row;
     - decode: the M codewords are widened to float32 and summed in ascending
       m, the accumulator starting from the m = 0 codeword (not from +0.0);
       the sum is multiplied by the row's scale in float32; the result is
@@ -48,7 +49,8 @@ import numpy as np
 
 __all__ = [
     "check_format", "decode", "decode_rows", "product", "forward",
-    "forward_rows", "within_tolerance", "bits_per_weight", "packed_bits_per_weight",
+    "forward_rows", "within_tolerance", "bits_per_weight", "stored_bits_per_weight",
+    "packed_bits_per_weight",
 ]
 
 
@@ -150,6 +152,15 @@ def within_tolerance(y, y_ref, bound, rel: float = 1e-2) -> np.ndarray:
 def bits_per_weight(out_features: int, in_features: int, M: int, B: int, g: int) -> float:
     """Closed form: code bits M*B/g, plus 16-bit codebooks and per-row scales amortised."""
     return (M * B / g
+            + 16.0 * M * (2 ** B) * g / (out_features * in_features)
+            + 16.0 / in_features)
+
+
+def stored_bits_per_weight(out_features: int, in_features: int, M: int, B: int, g: int) -> float:
+    """As bits_per_weight, but with each code in its storage element: one byte
+    per code for B <= 8, two bytes for 8 < B <= 16 (codes are not bit-packed)."""
+    code_bits = 8 * ((B + 7) // 8)
+    return (M * code_bits / g
             + 16.0 * M * (2 ** B) * g / (out_features * in_features)
             + 16.0 / in_features)
 

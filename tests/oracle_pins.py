@@ -105,11 +105,18 @@ def _special_codebooks(rng, M, B, g):
 def pin_brute_force_decode(impl):
     """Vectorised decode == exact per-element IEEE emulation, bit for bit."""
     rng = np.random.default_rng(12345)
-    for (M, B, g, out, J) in ((2, 8, 8, 3, 4), (1, 16, 8, 2, 3), (1, 16, 16, 2, 2),
-                              (3, 8, 4, 2, 3), (1, 8, 1, 4, 5)):
+    for (M, B, g, out, J, span) in ((2, 8, 8, 3, 4, 64), (1, 16, 8, 2, 3, 64),
+                                    (1, 16, 16, 2, 2, 64), (3, 8, 4, 2, 3, 64),
+                                    (1, 8, 1, 4, 5, 64),
+                                    # general schemes: more codebooks, wider codes
+                                    (4, 8, 8, 2, 3, 256), (8, 8, 16, 2, 2, 256),
+                                    (1, 12, 8, 3, 3, 4096), (2, 12, 16, 2, 2, 4096),
+                                    (3, 10, 8, 2, 3, 1024), (5, 16, 8, 2, 2, 65536)):
         books = _special_codebooks(rng, M, B, g)
-        codes = rng.integers(0, min(2 ** B, 64), size=(out, J, M)).astype(
+        codes = rng.integers(0, min(2 ** B, span), size=(out, J, M)).astype(
             np.uint8 if B == 8 else np.uint16)
+        if span > 256:
+            codes[0, 0, :] = 2 ** B - 1   # the last codeword of every codebook
         scales = rng.uniform(0.5, 1.5, size=out).astype(np.float16)
         scales[0] = np.float16(0.0009765625)   # push products into the subnormal range
         with np.errstate(over="ignore"):
@@ -258,6 +265,18 @@ def pin_bits_per_weight(impl):
         measured = impl.packed_bits_per_weight(codes, books, scales)
         closed = impl.bits_per_weight(out, n_in, M, B, g)
         assert abs(measured - closed) <= 1e-12 * closed, (out, n_in, M, B, g, measured, closed)
+    # codes wider than 8 bits sit in 16-bit elements: the stored size follows
+    # the container, and equals the nominal one when B fills whole bytes
+    for (out, n_in, M, B, g) in ((64, 128, 1, 12, 8), (32, 256, 2, 10, 16), (16, 64, 3, 8, 8),
+                                 (16, 64, 2, 16, 16), (8, 64, 8, 9, 8)):
+        codes = np.zeros((out, n_in // g, M), dtype=np.uint8 if B == 8 else np.uint16)
+        books = np.zeros((M, 2 ** B, g), dtype=np.float16)
+        scales = np.zeros(out, dtype=np.float16)
+        measured = impl.packed_bits_per_weight(codes, books, scales)
+        stored = impl.stored_bits_per_weight(out, n_in, M, B, g)
+        assert abs(measured - stored) <= 1e-12 * stored, (out, n_in, M, B, g, measured, stored)
+        nominal = impl.bits_per_weight(out, n_in, M, B, g)
+        assert (abs(stored - nominal) <= 1e-12 * nominal) == (B % 8 == 0)
     # 2 code bits per weight against 16-bit weights: the "up to ~8x" compression
     big = impl.bits_per_weight(1 << 20, 1 << 20, 2, 8, 8)
     assert abs(16 / big - 8.0) < 1e-3

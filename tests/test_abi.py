@@ -69,7 +69,8 @@ def test_null_layer_pointer(fn):
 @pytest.mark.parametrize("fn", sorted(ENTRY))
 @pytest.mark.parametrize("case,status", [
     (dict(codes=0), 1), (dict(books=0), 1), (dict(scales=0), 1),
-    (dict(M=3), 3), (dict(B=12), 3), (dict(g=4), 3), (dict(M=1, B=8), 3), (dict(M=2, B=16), 3),
+    (dict(M=0), 3), (dict(M=9), 3), (dict(B=7), 3), (dict(B=17), 3), (dict(g=4), 3),
+    (dict(g=32), 3), (dict(M=-1), 3),
     (dict(out=0), 2), (dict(n_in=0), 2), (dict(n_in=100), 2), (dict(out=-5), 2),
     (dict(reserved=1), 2), (dict(out=1 << 40), 2),
     (dict(M=1, B=16, g=16, n_in=136), 2),
@@ -124,7 +125,7 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_batched_validation():
     lib = _lib.load_library()
     n = 2
-    structs = (_lib.AqlmLayerStruct * n)(_layer(), _layer(M=3))
+    structs = (_lib.AqlmLayerStruct * n)(_layer(), _layer(M=9))
     xs = (ctypes.c_void_p * n)(FAKE, FAKE)
     ys = (ctypes.c_void_p * n)(FAKE, FAKE + 0x1000)
     f = lib.aqlm_gemv_batched
@@ -144,3 +145,14 @@ def test_batched_validation():
     # no-ops launch nothing
     assert f(good, xs, ys, 0, 1, None) == 0
     assert f(good, xs, ys, n, 0, None) == 0
+
+
+@pytest.mark.parametrize("M,B,g", [(1, 8, 8), (3, 8, 8), (8, 8, 16), (1, 12, 8), (2, 12, 16),
+                                   (2, 16, 8), (8, 16, 16), (4, 9, 8), (5, 15, 16)])
+def test_general_schemes_accepted(M, B, g):
+    """Every M in 1..8, B in 8..16, g in {8, 16} passes validation (batch 0 launches nothing)."""
+    s = _layer(M=M, B=B, g=g, n_in=16 * g)
+    for fn in ("aqlm_gemv", "aqlm_gemm"):
+        assert ENTRY[fn](s, FAKE, 0, FAKE) == 0
+    # the same descriptor with a bad pointer is still rejected before any launch
+    assert ENTRY["aqlm_gemv"](_layer(M=M, B=B, g=g, n_in=16 * g, codes=MISALIGNED), FAKE, 1, FAKE) == 4

@@ -1,0 +1,95 @@
+"""GPU parity for the general schemes (M = 1..8 codebooks, B = 8..16 code bits,
+g = 8 or 16), which run the library's general kernels: aqlm_dequant bit for
+bit against the CPU oracle, aqlm_gemv / aqlm_gemm within the product
+tolerance, one-hot probes, and every layer of the general_schemes workload at
+full size.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from additive_codebook_matmul_amd import workloads as WL
+from gpu_util import assert_bit_exact, assert_product, bits, dev_layer, dev_x
+
+pytestmark = pytest.mark.gpu
+
+S = WL.Scheme
+# one scheme per kernel instantiation (g x code width) plus the extremes of M and B
+SMALL_SCHEMES = [S(1, 8, 8), S(3, 8, 8), S(8, 8, 16), S(1, 12, 8), S(3, 10, 16), S(2, 16, 8),
+                 S(5, 9, 8), S(1, 8, 16)]
+# (out, groups): one row/group, ragged rows and groups, several 64-row / 64-input tiles
+SMALL_SHAPES = [(1, 1), (7, 5), (65, 9), (130, 17)]
+
+
+def _sid(s):
+    return s.name
+
+
+@pytest.mark.parametrize("scheme", SMALL_SCHEMES, ids=_sid)
+@pytest.mark.parametrize("out,J", SMALL_SHAPES)
+def test_general_small(scheme, out, J):
+    codes, books, scales, x = WL.small_case(out, J * scheme.g, scheme, 70, seed=out * 7 + J)
+    layer = dev_layer(codes, books, scales)
+    assert layer.general
+    w_ref = oracle.decode(codes, books, scales)
+    assert_bit_exact(layer.dequant().cpu().numpy(), w_ref, f"dequant {scheme.name} {out}x{J}")
+    for batch in (1, 3, 8):
+        y_ref, bound = oracle.product(x[:batch], w_ref)
+        assert_product(layer.gemv(dev_x(x[:batch])), y_ref, bound,
+                       f"gemv {scheme.name} {out}x{J} b{batch}")
+    for batch in (1, 9, 64, 70):
+        y_ref, bound = oracle.product(x[:batch], w_ref)
+        assert_product(layer.gemm(dev_x(x[:batch])), y_ref, bound,
+                       f"gemm {scheme.name} {out}x{J} b{batch}")
+
+
+@pytest.mark.parametrize("scheme", [S(4, 8, 8), S(2, 12, 16)], ids=_sid)
+def test_general_one_hot(scheme):
+    """x = e_i gives column i of W: exactly for the GEMM (it multiplies the
+    decoded float16 tile), within one float16 ulp for the GEMV."""
+    out, n_in = 200, 48 * scheme.g
+    codes, books, scales, _ = WL.small_case(out, n_in, scheme, 1, seed=11)
+    layer = dev_layer(codes, books, scales)
+    w_ref = oracle.decode(codes, books, scales)
+    cols = np.array([0, scheme.g - 1, scheme.g, n_in // 2, n_in - scheme.g, n_in - 1])
+    x = np.zeros((len(cols), n_in), dtype=np.float16)
+    x[np.arange(len(cols)), cols] = 1
+    ref = w_ref[:, cols].T
+    # equal as numbers (+0 and -0 compare equal: the zero products may flip a zero's sign)
+    assert np.array_equal(layer.gemm(dev_x(x)).cpu().numpy().astype(np.float32),
+                          ref.astype(np.float32))
+    y = layer.gemv(dev_x(x)).cpu().numpy().astype(np.float32)
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float32)
+    assert np.all(np.abs(y - ref.astype(np.float32)) <= ulp)
+
+
+@pytest.mark.parametrize("scheme", [S(3, 8, 8), S(1, 12, 16)], ids=_sid)
+def test_general_deterministic(scheme):
+    codes, books, scales, x = WL.small_case(300, 40 * scheme.g, scheme, 32, seed=5)
+    layer = dev_layer(codes, books, scales)
+    for fn, xb in ((layer.gemv, x[:8]), (layer.gemm, x)):
+        assert np.array_equal(bits(fn(dev_x(xb))), bits(fn(dev_x(xb)))), fn.__name__
+
+
+@functools.lru_cache(maxsize=2)
+def _layer_data(lname):
+    layer = next(l for l in WL.WORKLOADS["general_schemes"].layers if l.name == lname)
+    return layer, WL.make_layer(layer)
+
+
+@pytest.mark.parametrize("lname", [l.name for l in WL.WORKLOADS["general_schemes"].layers])
+def test_general_workload(lname):
+    layer, d = _layer_data(lname)
+    dl = dev_layer(d.codes, d.codebooks, d.scales)
+    w_ref = oracle.decode(d.codes, d.codebooks, d.scales)
+    assert_bit_exact(dl.dequant().cpu().numpy(), w_ref, f"dequant {lname}")
+    for batch in WL.WORKLOADS["general_schemes"].batches:
+        x = WL.make_x(layer, batch)
+        y_ref, bound = oracle.product(x, w_ref)
+        y = dl.gemv(dev_x(x)) if batch <= 8 else dl.gemm(dev_x(x))
+        assert_product(y, y_ref, bound, f"{lname} b{batch}")
+    del dl
+    torch.cuda.empty_cache()

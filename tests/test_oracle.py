@@ -32,6 +32,7 @@ def _impl(decode_rows=None, product=None):
 
     ns.decode_rows, ns.decode, ns.forward, ns.product = dr, decode, forward, pr
     ns.bits_per_weight, ns.packed_bits_per_weight = O.bits_per_weight, O.packed_bits_per_weight
+    ns.stored_bits_per_weight = O.stored_bits_per_weight
     return ns
 
 
@@ -143,6 +144,22 @@ def m_scale_by_group(codes, books, scales, rows):
     return acc.astype(np.float16).reshape(len(rows), -1)
 
 
+def m_low_byte_codes(codes, books, scales, rows):
+    # wide codes truncated to their low byte
+    c = np.asarray(codes)
+    return O.decode_rows((c.astype(np.int64) & 0xFF).astype(c.dtype), books, scales, rows)
+
+
+def m_first_two_codebooks(codes, books, scales, rows):
+    rows = np.asarray(rows)
+    g = _gather(codes, books, rows)
+    acc = g[0]
+    for t in g[1:2]:
+        acc = acc + t
+    acc = acc * np.asarray(scales)[rows].astype(np.float32)[:, None, None]
+    return acc.astype(np.float16).reshape(len(rows), -1)
+
+
 def p_drop_last_column(x, w16):
     x = np.asarray(x)[:, :-1]
     w16 = np.asarray(w16)[:, :-1]
@@ -175,6 +192,8 @@ MUTANTS = {
     "flush_subnormals": _impl(decode_rows=m_flush_subnormals),
     "truncating_round": _impl(decode_rows=m_truncate_round),
     "scale_indexed_by_group": _impl(decode_rows=m_scale_by_group),
+    "wide_codes_low_byte": _impl(decode_rows=m_low_byte_codes),
+    "first_two_codebooks_only": _impl(decode_rows=m_first_two_codebooks),
     "product_drops_last_column": _impl(product=p_drop_last_column),
     "product_rows_reversed": _impl(product=p_transposed_rows),
     "product_accumulates_in_fp16": _impl(product=p_fp32_accumulate_in_fp16),
