@@ -41,6 +41,15 @@ hipError_t launch_gemv_general(const LayerDesc &L, const uint16_t *x, int batch,
                                hipStream_t stream);
 hipError_t launch_gemm_general(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                                hipStream_t stream);
+// Matrix-core 2x8 GEMV for 1..8 activation rows (gemv_mfma.hip).
+bool gemv_2x8_mfma_fits(const LayerDesc &L, int batch);
+hipError_t launch_gemv_2x8_mfma(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
+                                hipStream_t stream);
+// Grouped form: launches every layer that gemv_2x8_mfma_fits accepts and sets
+// done[i] for it; the caller launches the rest.
+hipError_t launch_gemv_2x8_mfma_batched(const LayerDesc *Ls, const uint16_t *const *xs,
+                                        uint16_t *const *ys, int n, int batch, bool *done,
+                                        hipStream_t stream);
 hipError_t launch_gemv_batched(const LayerDesc *Ls, const uint16_t *const *xs,
                                uint16_t *const *ys, int n, int batch, hipStream_t stream);
 

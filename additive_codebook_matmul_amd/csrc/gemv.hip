@@ -13,6 +13,8 @@
 // slice of x, and the per-lane partial sums are reduced across the
 // wavefront with DPP in a fixed order. Generic path: one group per lane per
 // step, for rows whose code bytes are not a multiple of 16.
+#include <vector>
+
 #include "aqlm_device.hpp"
 
 namespace aqlm {
@@ -535,6 +537,7 @@ hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int batch, uint1
 
 hipError_t launch_gemv(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
                        hipStream_t stream) {
+  if (gemv_2x8_mfma_fits(L, batch)) return launch_gemv_2x8_mfma(L, x, batch, y, stream);
   switch (L.scheme) {
     case Scheme::k2x8: return launch_scheme<Scheme::k2x8>(L, x, batch, y, stream);
     case Scheme::k1x16: return launch_scheme<Scheme::k1x16>(L, x, batch, y, stream);
@@ -549,10 +552,25 @@ hipError_t launch_gemv_batched(const LayerDesc *Ls, const uint16_t *const *xs,
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  // layers the grouped kernel serves, bucketed by configuration; the rest run alone
+  // 2x8 layers the matrix-core kernel serves go to it, grouped
+  bool done_fixed[64];
+  std::vector<char> done_heap;
+  bool *done = done_fixed;
+  if (n > 64) {
+    done_heap.assign(n, 0);
+    done = reinterpret_cast<bool *>(done_heap.data());
+  }
+  for (int i = 0; i < n; ++i) done[i] = false;
+  {
+    const hipError_t e = launch_gemv_2x8_mfma_batched(Ls, xs, ys, n, batch, done, stream);
+    if (e != hipSuccess) return e;
+  }
+  // other layers the grouped lookup kernel serves, bucketed by configuration;
+  // the rest run alone
   GroupArgs buckets[6];
   for (int c = 0; c < 6; ++c) buckets[c].n = 0;
   for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
     const LayerDesc &L = Ls[i];
     const int64_t chunks = L.groups / 8;
     const bool fits32 = (L.out + 4096) * chunks * 16 < ((int64_t)1 << 31) &&

@@ -36,9 +36,9 @@ METRIC = "AQLM GEMV µs/layer + achieved HBM GB/s (% of peak), Llama-2-7B shapes
 WORKLOAD = "llama2_7b_2x8"
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
-GEMV_KERNEL = "gemv_2x8_group_kernel (grouped 2x8 GEMV, batch 1, one code chunk per lane)"
+GEMV_KERNEL = "gemv_2x8_mfma_group_kernel (grouped 2x8 GEMV on the matrix cores, batch 1)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_2x8_llama2_7b_b1_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "additive_codebook_matmul_amd", "csrc", "gemv.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "additive_codebook_matmul_amd", "csrc", "gemv_mfma.hip")
 
 
 def _parse():
