@@ -42,6 +42,11 @@ __device__ __forceinline__ uint4 buf_load16_nt(Rsrc r, uint32_t off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint2 buf_load8(Rsrc r, uint32_t off) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
 // 16-bit load zero-extended into its own 32-bit register (kept unpacked so a
 // refill never has to merge into a register another value lives in).
 __device__ __forceinline__ uint32_t buf_load_u16(Rsrc r, uint32_t off) {

@@ -1,18 +1,22 @@
 // Batched product y = x . W^T on the matrix cores: tiles of W are decoded on
 // chip straight into MFMA operand registers and multiplied with float16
-// activations by v_mfma_f32_32x32x16_f16 (float32 accumulation). W is never
-// written to memory.
+// activations (float32 accumulation). W is never written to memory.
 //
-// Block: 4 wavefronts. Each wavefront owns 64 output rows (two 32-row MFMA
-// tiles) and the block's BN = 64 activation rows (two 32-column tiles), so a
-// block covers 256 x 64 outputs. The K loop walks 8 groups at a time (64
-// inputs for g = 8, 128 for g = 16):
-//   * activations for the next K block are loaded from HBM into registers
-//     and then written to a double-buffered LDS tile (rows padded by 16 bytes
-//     so that 32 lanes reading one column hit distinct banks);
+// Wide tiles (more than kSkinnyMaxBatch activation rows, gemm_wide_kernel):
+// 4 wavefronts, each owning 64 output rows (two 32-row tiles of
+// v_mfma_f32_32x32x16_f16) and the block's 32*NI activation rows (NI 32-column
+// tiles), so a block covers 256 x 32*NI outputs and every decoded operand is
+// used NI times. The K loop walks 8 groups at a time (64 inputs for g = 8,
+// 128 for g = 16):
+//   * codes are loaded kWideCodeDepth K blocks ahead (a static register ring,
+//     the loop being unrolled to match), activations two K blocks ahead into
+//     registers, then written to a double-buffered LDS tile (rows padded by 16
+//     bytes so that 32 lanes reading one column hit distinct banks). Every
+//     load is an unconditional buffer load (out-of-range offsets read zero),
+//     so the compiler keeps exact wait counts;
 //   * each lane decodes its rows' groups into an 8-half A operand: the sum of
-//     the codewords in packed fp16 (2x8: the two codewords come from LDS;
-//     1x16: one 16-byte gather from the L2-resident codebook);
+//     the codewords in packed fp16 (2x8: the two codewords come from an 8 KiB
+//     LDS copy; 1x16: one 16-byte gather from the L2-resident codebook);
 //   * the row scale multiplies the float32 accumulator in the epilogue.
 // The MFMA K index of every lane element is paired identically in A and B, so
 // any assignment of groups to MFMA steps gives the same sum; for g = 8 the two
@@ -27,25 +31,29 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kBM = 256;  // output rows per block
-constexpr int kBN = 64;   // activation rows per block
 constexpr int kKG = 8;    // groups per K block
+constexpr int kWideCodeDepth = 4;
+constexpr uint32_t kWideOOB = 0x80000000u;
 
-template <Scheme S>
-struct GemmCfg {
+template <Scheme S, int NI>
+struct WideCfg {
   static constexpr int G = group_size(S);
-  static constexpr int KI = kKG * G;         // inputs per K block
-  static constexpr int ROW_HALVES = KI + 8;  // padded LDS row of the activation tile
-  static constexpr int TILE_HALVES = kBN * ROW_HALVES;
-  static constexpr int XVEC = kBN * KI / 8;  // 16-byte vectors per activation tile
-  static constexpr int XPT = XVEC / kBlock;  // vectors staged per thread
+  static constexpr int BN = 32 * NI;            // activation rows per block
+  static constexpr int KI = kKG * G;            // inputs per K block
+  static constexpr int ROW_HALVES = KI + 8;     // padded LDS row of the activation tile
+  static constexpr int TILE_HALVES = BN * ROW_HALVES;
+  static constexpr int XPT = BN * KI / 8 / kBlock;  // 16-byte activation vectors per thread
+  static constexpr int CWORDS = G == 8 ? 2 : 4;     // code words per lane, row tile and K block
 };
 
-template <Scheme S, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void gemm_kernel(
+template <Scheme S, bool ALIGNED, int NI>
+__global__ __launch_bounds__(kBlock) void gemm_wide_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
-    uint16_t *__restrict__ y, int out, int in, int groups, int batch) {
-  using C = GemmCfg<S>;
+    uint16_t *__restrict__ y, int out, int in, int groups, int batch, uint32_t codes_bytes,
+    uint32_t x_bytes) {
+  using C = WideCfg<S, NI>;
+  constexpr int KD = kWideCodeDepth;
   __shared__ uint4 lds_books[S == Scheme::k2x8 ? 512 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[2][C::TILE_HALVES];
 
@@ -54,33 +62,60 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(
   const int half = lane >> 5;  // which 8 K values of the MFMA step this lane feeds
   const int l32 = lane & 31;
   const int row0 = blockIdx.x * kBM + wave * 64;
-  const int tok0 = blockIdx.y * kBN;
-  const int64_t row_bytes = (int64_t)groups * 2;
+  const int tok0 = blockIdx.y * C::BN;
+  const uint32_t row_bytes = (uint32_t)groups * 2u;
   const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
-
-  if constexpr (S == Scheme::k2x8) {
-    for (int i = threadIdx.x; i < 512; i += kBlock) lds_books[i] = gbooks[i];
-  }
-
+  const Rsrc crs = make_rsrc(codes, codes_bytes);
+  const Rsrc xrs = make_rsrc(x, x_bytes);
   const int nkb = (groups + kKG - 1) / kKG;
 
-  // Activation staging: thread t moves vectors t, t + 256, ... of the tile.
-  uint4 xr[C::XPT];
-  auto load_x = [&](int kb) {
+  // Codes of the lane's two row tiles for K block kb: g = 8 lanes need 4
+  // groups (8 bytes) each, g = 16 lanes all 8 groups (16 bytes).
+  auto load_codes = [&](int kb, uint32_t (&cw)[2][C::CWORDS]) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const uint32_t rowoff = (uint32_t)(row0 + mi * 32 + l32) * row_bytes;
+      const bool ok = kb < nkb;
+      if constexpr (ALIGNED) {
+        if constexpr (C::G == 8) {
+          const uint2 v = buf_load8(crs, ok ? rowoff + (uint32_t)kb * 16u + half * 8u : kWideOOB);
+          cw[mi][0] = v.x;
+          cw[mi][1] = v.y;
+        } else {
+          const uint4 v = buf_load16(crs, ok ? rowoff + (uint32_t)kb * 16u : kWideOOB);
+          cw[mi][0] = v.x;
+          cw[mi][1] = v.y;
+          cw[mi][2] = v.z;
+          cw[mi][3] = v.w;
+        }
+      } else {
+        // rows whose codes are not 16-byte aligned: one 16-bit code at a time
+        constexpr int NQ = C::G == 8 ? 4 : 8;
+#pragma unroll
+        for (int w = 0; w < C::CWORDS; ++w) cw[mi][w] = 0;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) {
+          const int gidx = kb * kKG + (C::G == 8 ? half * 4 : 0) + qq;
+          const uint32_t c =
+              buf_load_u16(crs, (ok && gidx < groups) ? rowoff + (uint32_t)gidx * 2u : kWideOOB);
+          cw[mi][qq >> 1] |= c << ((qq & 1) * 16);
+        }
+      }
+    }
+  };
+  // Activations of K block kb: thread t moves vectors t, t + 256, ... of the tile.
+  auto load_x = [&](int kb, uint4 (&xr)[C::XPT]) {
 #pragma unroll
     for (int i = 0; i < C::XPT; ++i) {
       const int v = threadIdx.x + i * kBlock;
       const int t = v / (C::KI / 8);
       const int kv = v - t * (C::KI / 8);
-      const int tok = tok0 + t;
       const int col = kb * C::KI + kv * 8;
-      if (tok < batch && col < in)
-        xr[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)tok * in + col);
-      else
-        xr[i] = make_uint4(0, 0, 0, 0);
+      const uint32_t off = (uint32_t)(tok0 + t) * (uint32_t)in * 2u + (uint32_t)col * 2u;
+      xr[i] = buf_load16(xrs, col < in ? off : kWideOOB);
     }
   };
-  auto store_x = [&](int buf) {
+  auto store_x = [&](int buf, const uint4 (&xr)[C::XPT]) {
 #pragma unroll
     for (int i = 0; i < C::XPT; ++i) {
       const int v = threadIdx.x + i * kBlock;
@@ -90,69 +125,18 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(
     }
   };
 
-  // Codes of the lane's two rows for one K block: g = 8 lanes need 4 groups
-  // (8 bytes) each, g = 16 lanes need all 8 groups (16 bytes).
-  auto load_codes = [&](int kb, int mi, uint32_t (&cw)[4]) {
-    const int row = row0 + mi * 32 + l32;
-    cw[0] = cw[1] = cw[2] = cw[3] = 0;
-    if (row >= out) return;
-    const uint8_t *rp = codes + (int64_t)row * row_bytes;
-    if constexpr (ALIGNED) {
-      if constexpr (C::G == 8) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(rp + (int64_t)kb * 16 + half * 8);
-        cw[0] = v.x;
-        cw[1] = v.y;
-      } else {
-        const uint4 v = *reinterpret_cast<const uint4 *>(rp + (int64_t)kb * 16);
-        cw[0] = v.x;
-        cw[1] = v.y;
-        cw[2] = v.z;
-        cw[3] = v.w;
-      }
-    } else {
-      const uint16_t *rp16 = reinterpret_cast<const uint16_t *>(rp);
-      if constexpr (C::G == 8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int gidx = kb * kKG + half * 4 + q;
-          const uint32_t c = gidx < groups ? rp16[gidx] : 0u;
-          cw[q >> 1] |= c << ((q & 1) * 16);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int gidx = kb * kKG + q;
-          const uint32_t c = gidx < groups ? rp16[gidx] : 0u;
-          cw[q >> 1] |= c << ((q & 1) * 16);
-        }
-      }
-    }
-  };
-
-  float16_t acc[2][2];
+  float16_t acc[2][NI];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  load_x(0);
-  store_x(0);
-  __syncthreads();
-
-  uint32_t cw[2][4];
-  load_codes(0, 0, cw[0]);
-  load_codes(0, 1, cw[1]);
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load_x(kb + 1);
-    uint32_t cwn[2][4];
-    if (kb + 1 < nkb) {
-      load_codes(kb + 1, 0, cwn[0]);
-      load_codes(kb + 1, 1, cwn[1]);
-    }
+  // one K block from LDS tile `buf` with codes cw; MASK zeroes the operands of
+  // groups past the end of the row (a partial last K block)
+  auto compute = [&](auto masked, int kb, int buf, const uint32_t (&cw)[2][C::CWORDS]) {
+    constexpr bool MASK = decltype(masked)::value;
     const uint16_t *xt = lds_x[buf];
     constexpr int STEPS = C::G == 8 ? 4 : 8;
 #pragma unroll
@@ -162,8 +146,7 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(
       uint4 a[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
-        const int q = C::G == 8 ? s : s;  // index of the group within the lane's code words
-        const uint32_t code = (cw[mi][q >> 1] >> ((q & 1) * 16)) & 0xFFFFu;
+        const uint32_t code = (cw[mi][s >> 1] >> ((s & 1) * 16)) & 0xFFFFu;
         if constexpr (S == Scheme::k2x8) {
           a[mi] = hadd8(lds_books[code & 0xFF], lds_books[256 + (code >> 8)]);
         } else if constexpr (S == Scheme::k1x16) {
@@ -171,35 +154,71 @@ __global__ __launch_bounds__(kBlock) void gemm_kernel(
         } else {
           a[mi] = gbooks[2 * code + half];
         }
+        if constexpr (MASK) {
+          const int gidx = kb * kKG + (C::G == 8 ? half * 4 + s : s);
+          if (gidx >= groups) a[mi] = make_uint4(0, 0, 0, 0);
+        }
       }
-      uint4 bx[2];
+      uint4 bx[NI];
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
         bx[ni] = *reinterpret_cast<const uint4 *>(&xt[(ni * 32 + l32) * C::ROW_HALVES + kcol]);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               __builtin_bit_cast(half8_t, a[mi]), __builtin_bit_cast(half8_t, bx[ni]),
               acc[mi][ni], 0, 0, 0);
     }
-    if (kb + 1 < nkb) {
-      store_x(buf ^ 1);
+  };
+
+  // Prologue: codes of K blocks 0 .. KD-1, activations of K blocks 0 and 1,
+  // the 2x8 codebooks, then K block 0's activations into LDS.
+  uint32_t cw[KD][2][C::CWORDS];
+  uint4 xr[2][C::XPT];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cw[mi][q] = cwn[mi][q];
-    }
-    __syncthreads();
+  for (int i = 0; i < KD; ++i) load_codes(i, cw[i]);
+  load_x(0, xr[0]);
+  load_x(1, xr[1]);
+  if constexpr (S == Scheme::k2x8) {
+    for (int i = threadIdx.x; i < 512; i += kBlock) lds_books[i] = gbooks[i];
   }
+  store_x(0, xr[0]);
+  __syncthreads();
+
+  const bool tail_partial = groups % kKG != 0;
+  // K block kb (code slot K = kb % KD, activation slot kb % 2): prefetch
+  // activations of kb + 2, compute, write kb + 1's activations to the other
+  // LDS buffer, refill code slot K with kb + KD.
+  auto iter = [&](int kb, auto kc) {
+    constexpr int K = decltype(kc)::value;
+    load_x(kb + 2, xr[K & 1]);
+    if (tail_partial && kb == nkb - 1)
+      compute(std::true_type{}, kb, K & 1, cw[K]);
+    else
+      compute(std::false_type{}, kb, K & 1, cw[K]);
+    store_x((K + 1) & 1, xr[(K + 1) & 1]);
+    load_codes(kb + KD, cw[K]);
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb + 4 <= nkb; kb += 4) {
+    iter(kb, std::integral_constant<int, 0>{});
+    iter(kb + 1, std::integral_constant<int, 1>{});
+    iter(kb + 2, std::integral_constant<int, 2>{});
+    iter(kb + 3, std::integral_constant<int, 3>{});
+  }
+  if (kb < nkb) iter(kb, std::integral_constant<int, 0>{});
+  if (kb + 1 < nkb) iter(kb + 1, std::integral_constant<int, 1>{});
+  if (kb + 2 < nkb) iter(kb + 2, std::integral_constant<int, 2>{});
 
   // Epilogue: lane holds column l32 of each 32x32 tile; register r is row
   // 8*(r/4) + 4*half + r%4.
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
+    for (int ni = 0; ni < NI; ++ni) {
       const int tok = tok0 + ni * 32 + l32;
       if (tok >= batch) continue;
 #pragma unroll
@@ -543,22 +562,48 @@ bool skinny_fits(const LayerDesc &L, int64_t batch, int nt) {
   return code_span < (int64_t(1) << 32) && x_span < (int64_t(1) << 32);
 }
 
+// Activation rows per wide block, 32 * NI. The 1x16 schemes gather their
+// codewords from L2, so a wider block (each gather feeding more MFMAs) pays;
+// 2x8 decodes from LDS and prefers the smaller register footprint (two waves
+// per SIMD instead of one).
+template <Scheme S>
+constexpr int wide_ni() { return S == Scheme::k2x8 ? 2 : 4; }
+
+// 32-bit byte offsets of the wide kernel: codes of 256 rows past the end and
+// activations of a whole block past the end must stay below 2^32.
+bool wide_fits(const LayerDesc &L, int64_t batch, int ni) {
+  const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
+  return (L.out + kBM) * row_bytes + 4096 < (int64_t(1) << 31) &&
+         (batch + 32 * ni) * L.in * 2 + 4096 < (int64_t(1) << 31);
+}
+
+template <Scheme S, int NI>
+hipError_t launch_wide(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
+                       hipStream_t stream) {
+  const int out = (int)L.out, in = (int)L.in, groups = (int)L.groups;
+  const dim3 grid((out + kBM - 1) / kBM, (unsigned)((batch + 32 * NI - 1) / (32 * NI)));
+  const uint8_t *codes = static_cast<const uint8_t *>(L.codes);
+  const uint32_t codes_bytes = (uint32_t)(L.out * L.groups * kCodeBytesPerGroup);
+  const uint32_t x_bytes = (uint32_t)(batch * L.in * 2);
+  if (groups % kKG == 0)
+    hipLaunchKernelGGL((gemm_wide_kernel<S, true, NI>), grid, dim3(kBlock), 0, stream, codes,
+                       L.books, L.scales, x, y, out, in, groups, (int)batch, codes_bytes, x_bytes);
+  else
+    hipLaunchKernelGGL((gemm_wide_kernel<S, false, NI>), grid, dim3(kBlock), 0, stream, codes,
+                       L.books, L.scales, x, y, out, in, groups, (int)batch, codes_bytes, x_bytes);
+  return hipGetLastError();
+}
+
 template <Scheme S>
 hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                          hipStream_t stream) {
   if (batch <= 16 && skinny_fits(L, batch, 1)) return launch_skinny<S, 1>(L, x, batch, y, stream);
   if (batch <= kSkinnyMaxBatch && skinny_fits(L, batch, 2))
     return launch_skinny<S, 2>(L, x, batch, y, stream);
-  const int out = (int)L.out, in = (int)L.in, groups = (int)L.groups;
-  const dim3 grid((out + kBM - 1) / kBM, (unsigned)((batch + kBN - 1) / kBN));
-  const uint8_t *codes = static_cast<const uint8_t *>(L.codes);
-  if (groups % kKG == 0)
-    hipLaunchKernelGGL((gemm_kernel<S, true>), grid, dim3(kBlock), 0, stream, codes, L.books,
-                       L.scales, x, y, out, in, groups, (int)batch);
-  else
-    hipLaunchKernelGGL((gemm_kernel<S, false>), grid, dim3(kBlock), 0, stream, codes, L.books,
-                       L.scales, x, y, out, in, groups, (int)batch);
-  return hipGetLastError();
+  if (wide_fits(L, batch, wide_ni<S>())) return launch_wide<S, wide_ni<S>()>(L, x, batch, y, stream);
+  // sizes past the 32-bit offsets of the tiled kernels: the general kernel
+  // (64-bit indexing, exact fp16 weight tiles)
+  return launch_gemm_general(L, x, batch, y, stream);
 }
 
 }  // namespace
