@@ -2,13 +2,14 @@
 //
 // The lookup GEMV spends twelve VALU operations per group (four address
 // permutes, eight fp16 dot2), so it is issue-bound far below HBM speed. Here
-// the dot products run on v_mfma_f32_16x16x32_f16 instead: a codeword read
-// from LDS is fed to the MFMA as A operand as it is, one MFMA per codebook, so
-// the sum over codebooks and groups is accumulated in float32 with no fp16
-// rounding of the codeword sum. The activation rows are the B operand (16
-// MFMA columns, the first BATCH of them used). A group then costs 2/64 of an
-// address permute per lane and two 16-byte LDS reads; the kernel is bound by
-// LDS and HBM bandwidth rather than by VALU issue.
+// the dot products run on v_mfma_f32_16x16x32_f16 instead: the two codewords
+// of a group are read from LDS, added in fp16 (one packed add per pair of
+// weights, as in the batched GEMM's tiles) and fed to one MFMA as A operand;
+// the sum over groups is accumulated in float32 and the row scale applied to
+// it. The activation rows are the B operand (16 MFMA columns, the first BATCH
+// of them used). A group then costs 2/64 of an address permute per lane, two
+// 16-byte LDS reads and half an MFMA step; the kernel is bound by LDS and HBM
+// bandwidth rather than by VALU issue.
 //
 // Layout of the work:
 //   * a workgroup (8 wavefronts) owns tiles of 16 output rows; its
@@ -26,6 +27,10 @@
 //   * the activations are copied to LDS once per workgroup (rows padded by 16
 //     bytes); B fragment reads of one activation row are broadcasts;
 //   * codes of NBUF tiles ahead are in flight (buffer loads, non-temporal).
+//     NBUF is 1 when no block has more than two tiles: a prefetch past the
+//     last tile is a load with an out-of-range offset, which returns zero but
+//     still occupies the texture-address unit that the real loads of every
+//     wave on the CU queue behind.
 #include "aqlm_device.hpp"
 
 #include <atomic>
@@ -90,7 +95,9 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
   const uint4 book_v = reinterpret_cast<const uint4 *>(L.books)[tm * 256 + tc];
   const int nxv = batch * (in / 8);  // 16-byte activation vectors
   const Rsrc rx = make_rsrc(L.x, (uint32_t)nxv * 16u);
-  constexpr int kXPT = 4;            // activation vectors per thread and pass
+  // activation vectors per thread and pass: enough for BATCH rows of the
+  // longest input the class serves (MAXC * 8 waves * 32 groups), at most 4
+  constexpr int kXPT = BATCH * MAXC / 2 < 1 ? 1 : (BATCH * MAXC / 2 > 4 ? 4 : BATCH * MAXC / 2);
   uint4 xv[kXPT];
 #pragma unroll
   for (int j = 0; j < kXPT; ++j) xv[j] = buf_load16(rx, (uint32_t)(tid + j * kMBlock) * 16u);
@@ -186,14 +193,16 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
             a1[u] = *reinterpret_cast<const uint4 *>(table + addrB);
             b[u] = *reinterpret_cast<const uint4 *>(xrow + (k * 32 + s) * 8);
           }
+          // two accumulators so that consecutive MFMAs are independent
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a0[u]),
-                                                          __builtin_bit_cast(half8_t, b[u]), acc0,
-                                                          0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a1[u]),
-                                                          __builtin_bit_cast(half8_t, b[u]), acc1,
-                                                          0, 0, 0);
+            const half8_t w = __builtin_bit_cast(half8_t, hadd8(a0[u], a1[u]));
+            if (u & 1)
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(w, __builtin_bit_cast(half8_t, b[u]),
+                                                            acc1, 0, 0, 0);
+            else
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(w, __builtin_bit_cast(half8_t, b[u]),
+                                                            acc0, 0, 0, 0);
           }
         }
       }
@@ -288,14 +297,18 @@ hipError_t launch_group(const MfmaGroup &G, int blocks, size_t lds, hipStream_t 
   return hipGetLastError();
 }
 
-// Chunk-per-wave class: MAXC >= ceil(chunks / 8), NBUF tiles of codes in flight.
+// Chunk-per-wave class: MAXC >= ceil(chunks / 8).
 int mfma_class(int64_t nch) {
-  if (nch <= 16) return 0;   // MAXC 2, NBUF 8
-  if (nch <= 32) return 1;   // MAXC 4, NBUF 4
-  if (nch <= 64) return 2;   // MAXC 8, NBUF 2
-  if (nch <= 128) return 3;  // MAXC 16, NBUF 2
+  if (nch <= 16) return 0;   // MAXC 2
+  if (nch <= 32) return 1;   // MAXC 4
+  if (nch <= 64) return 2;   // MAXC 8
+  if (nch <= 128) return 3;  // MAXC 16
   return -1;
 }
+
+// Tiles of codes in flight per wave: one when no block has more than two
+// tiles (a deeper prefetch would only issue out-of-range loads), else two.
+constexpr int nbuf_for(int max_tiles_per_block) { return max_tiles_per_block <= 2 ? 1 : 2; }
 
 int device_cus() {
   int dev = 0, cus = 256;
@@ -331,11 +344,12 @@ hipError_t launch_mfma_batch(const LayerDesc &L, const uint16_t *x, int batch, u
   if (blocks < min_blocks) blocks = min_blocks;
   MfmaLayer M{static_cast<const uint8_t *>(L.codes), L.books, L.scales, x, y, (int)L.out, (int)L.in,
               (int)L.groups, batch, 0, blocks};
+  const bool deep = nbuf_for((ntiles + blocks - 1) / blocks) == 2;
   switch (mfma_class(L.groups / 32)) {
-    case 0: return launch_one<BATCH, 2, 8>(M, stream);
-    case 1: return launch_one<BATCH, 4, 4>(M, stream);
-    case 2: return launch_one<BATCH, 8, 2>(M, stream);
-    case 3: return launch_one<BATCH, 16, 2>(M, stream);
+    case 0: return deep ? launch_one<BATCH, 2, 2>(M, stream) : launch_one<BATCH, 2, 1>(M, stream);
+    case 1: return deep ? launch_one<BATCH, 4, 2>(M, stream) : launch_one<BATCH, 4, 1>(M, stream);
+    case 2: return deep ? launch_one<BATCH, 8, 2>(M, stream) : launch_one<BATCH, 8, 1>(M, stream);
+    case 3: return deep ? launch_one<BATCH, 16, 2>(M, stream) : launch_one<BATCH, 16, 1>(M, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -343,7 +357,7 @@ hipError_t launch_mfma_batch(const LayerDesc &L, const uint16_t *x, int batch, u
 // Several layers in one launch, one class (chunks per wave) at a time: blocks
 // are split over the layers in proportion to their code bytes, at least one
 // tile per block and at most kMaxTilesPerBlock tiles per block.
-template <int BATCH, int MAXC, int NBUF>
+template <int BATCH, int MAXC>
 hipError_t launch_mfma_group(const LayerDesc *const *Ls, const uint16_t *const *xs,
                              uint16_t *const *ys, int n, int batch, hipStream_t stream) {
   MfmaGroup G;
@@ -359,7 +373,7 @@ hipError_t launch_mfma_group(const LayerDesc *const *Ls, const uint16_t *const *
   // every layer of a class up to its chunk count), the same for all layers
   double tile_work = 0;
   for (int i = 0; i < n; ++i) tile_work += (double)((Ls[i]->out + 15) / 16) * (double)Ls[i]->groups;
-  int begin = 0;
+  int begin = 0, max_per_block = 1;
   for (int i = 0; i < n; ++i) {
     const LayerDesc &L = *Ls[i];
     const int ntiles = (int)((L.out + 15) / 16);
@@ -369,21 +383,23 @@ hipError_t launch_mfma_group(const LayerDesc *const *Ls, const uint16_t *const *
     if (per_block < 1) per_block = 1;
     if (per_block > kMaxTilesPerBlock) per_block = kMaxTilesPerBlock;
     const int blocks = (ntiles + per_block - 1) / per_block;
+    if (per_block > max_per_block) max_per_block = per_block;
     G.layer[i] = MfmaLayer{static_cast<const uint8_t *>(L.codes), L.books, L.scales, xs[i], ys[i],
                            (int)L.out, (int)L.in, (int)L.groups, batch, begin, blocks};
     begin += blocks;
   }
-  return launch_group<BATCH, MAXC, NBUF>(G, begin, lds, stream);
+  return nbuf_for(max_per_block) == 2 ? launch_group<BATCH, MAXC, 2>(G, begin, lds, stream)
+                                      : launch_group<BATCH, MAXC, 1>(G, begin, lds, stream);
 }
 
 template <int BATCH>
 hipError_t mfma_group_batch(const LayerDesc *const *Ls, const uint16_t *const *xs,
                             uint16_t *const *ys, int n, int batch, int cls, hipStream_t stream) {
   switch (cls) {
-    case 0: return launch_mfma_group<BATCH, 2, 8>(Ls, xs, ys, n, batch, stream);
-    case 1: return launch_mfma_group<BATCH, 4, 4>(Ls, xs, ys, n, batch, stream);
-    case 2: return launch_mfma_group<BATCH, 8, 2>(Ls, xs, ys, n, batch, stream);
-    case 3: return launch_mfma_group<BATCH, 16, 2>(Ls, xs, ys, n, batch, stream);
+    case 0: return launch_mfma_group<BATCH, 2>(Ls, xs, ys, n, batch, stream);
+    case 1: return launch_mfma_group<BATCH, 4>(Ls, xs, ys, n, batch, stream);
+    case 2: return launch_mfma_group<BATCH, 8>(Ls, xs, ys, n, batch, stream);
+    case 3: return launch_mfma_group<BATCH, 16>(Ls, xs, ys, n, batch, stream);
   }
   return hipErrorInvalidValue;
 }
