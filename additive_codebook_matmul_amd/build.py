@@ -2,7 +2,8 @@
 
 Usage: python -m additive_codebook_matmul_amd.build   (or call build_library()).
 The library lands next to this file as libaqlm_mi355x.so; objects go under
-_build/. Every call recompiles from source.
+_build/. Every call recompiles from source. build_host_library() compiles the
+separate host GEMV library (libaqlm_host.so, g++ with OpenMP).
 """
 from __future__ import annotations
 
@@ -21,6 +22,8 @@ LIB_NAME = "libaqlm_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ("api.hip", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "general.hip")
 ARCH = "gfx950"
+HOST_SOURCE = "host_gemv.cpp"
+HOST_LIB_PATH = os.path.join(PKG_DIR, "libaqlm_host.so")
 
 
 def hipcc() -> str:
@@ -64,5 +67,20 @@ def build_library(verbose: bool = True) -> str:
     return LIB_PATH
 
 
+def build_host_library(verbose: bool = True) -> str:
+    cxx = os.environ.get("CXX") or shutil.which("g++") or "g++"
+    tmp = HOST_LIB_PATH + ".tmp"
+    cmd = [cxx, "-O3", "-std=c++17", "-fPIC", "-shared", "-fopenmp", "-fvisibility=hidden",
+           "-Wall", "-I", INCLUDE, os.path.join(CSRC, HOST_SOURCE), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"host library build failed:\n{res.stderr}")
+    os.replace(tmp, HOST_LIB_PATH)
+    if verbose:
+        print(f"built {HOST_LIB_PATH}", file=sys.stderr)
+    return HOST_LIB_PATH
+
+
 if __name__ == "__main__":
     build_library()
+    build_host_library()

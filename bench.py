@@ -15,7 +15,9 @@ Reported value: achieved HBM GB/s = (codes + x + y bytes of the seven layers)
 bracketed by device synchronisation. Also reported: microseconds per layer
 launched alone, the whole block as a single batched call, the roofline
 object of the dominant kernel (the grouped GEMV of the q,k,v and gate,up
-calls) and the CPU oracle timed on a bounded sample of the same workload.
+calls), the CPU oracle timed on a bounded sample of the same workload, and
+the host library's GEMV (aqlm_host_gemv, table lookup on the CPU cores) on the
+same seven layers.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -49,6 +51,8 @@ def _parse():
     p.add_argument("--layer-iters", type=int, default=200,
                    help="launches per layer for the per-layer timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-host-gemv", action="store_true",
+                   help="skip timing the host library's GEMV on the CPU cores")
     p.add_argument("--workload", default=WORKLOAD,
                    help="llama2_7b_2x8 (default: the headline step), or per-layer tables for "
                         "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, "
@@ -118,6 +122,32 @@ def cpu_baseline(layers_np, budget_s: float = 12.0):
         "sample": f"{done_layers} layer products of the seven Llama-2-7B 2x8 layers at batch 1 "
                   f"(whole passes over the layer set, {dt:.1f} s); numpy decode is single-threaded, "
                   f"the float64 product uses BLAS with up to {blas_threads} threads",
+    }
+
+
+def host_gemv_context(layers_np, budget_s: float = 2.0):
+    """The host library (aqlm_host_gemv) over the same seven layers at batch 1."""
+    from additive_codebook_matmul_amd import host
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    for (_, d, x, _) in layers_np:  # warm the code pages and the thread pool
+        host.host_gemv(d.codes, d.codebooks, d.scales, x, threads=threads)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for (_, d, x, _) in layers_np:
+            host.host_gemv(d.codes, d.codebooks, d.scales, x, threads=threads)
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / passes
+    step_bytes = sum(nb for (_, _, _, nb) in layers_np)
+    return {
+        "value": round(step_bytes / dt / 1e9, 3),
+        "unit": "GB/s",
+        "us_per_step": round(dt * 1e6, 1),
+        "threads": threads,
+        "isa": host.host_isa(),
+        "kind": "host library aqlm_host_gemv (float32 lookup tables for 8-bit codebooks)",
+        "sample": f"{passes} passes over the seven layers, codes in host memory",
     }
 
 
@@ -411,6 +441,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(layers_np)
+    if not args.no_host_gemv:
+        result["host_gemv"] = host_gemv_context(layers_np)
     print(json.dumps(result), flush=True)
 
 

@@ -16,8 +16,8 @@ FAKE = 0x10000      # a 16-byte aligned address that is never dereferenced
 MISALIGNED = 0x10008
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"AQLM_API\s+[\w\s\*]*?\b(aqlm_\w+)\s*\(", text)))
 
 
@@ -30,6 +30,18 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert lib.aqlm_abi_version() == _lib.ABI_VERSION
+
+
+def test_host_library_exports_every_declared_symbol():
+    from additive_codebook_matmul_amd import host
+    if not os.path.exists(host.HOST_LIB_PATH):
+        from additive_codebook_matmul_amd.build import build_host_library
+        build_host_library(verbose=False)
+    declared = _declared_functions(os.path.join(ROOT, "include", "aqlm_host.h"))
+    assert declared == sorted(host.HOST_EXPORTED_SYMBOLS)
+    lib = host.load_host_library()
+    for name in declared:
+        assert hasattr(lib, name), name
 
 
 def test_struct_layout_matches_header():
