@@ -193,3 +193,30 @@ def workload_bytes(layer: Layer, batch: int) -> Dict[str, int]:
         "x": batch * layer.in_features * 2,
         "y": batch * layer.out_features * 2,
     }
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the toy encoder: a dense float16 weight matrix and the seeded
+# starting indices of each codebook's k-means. Random draws only; the encoder's
+# arithmetic lives in the library and, separately, in the oracle.
+# ---------------------------------------------------------------------------
+def make_dense_weight(out_features: int, in_features: int, seed: int,
+                      std: float = 0.02) -> np.ndarray:
+    """A dense weight matrix [out, in]: N(0, std) drawn in float64, rounded to float16."""
+    rng = np.random.default_rng(seed)
+    return rng.normal(0.0, std, size=(out_features, in_features)).astype(np.float16)
+
+
+def kmeans_init_indices(n_vectors: int, K: int, M: int, seed: int) -> List[np.ndarray]:
+    """For each of M codebooks, K starting vector indices: K distinct indices
+    drawn uniformly when n_vectors >= K, otherwise a random permutation of all
+    vectors repeated to length K. int64, one array per codebook."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(M):
+        if n_vectors >= K:
+            idx = rng.choice(n_vectors, size=K, replace=False)
+        else:
+            idx = np.resize(rng.permutation(n_vectors), K)
+        out.append(np.ascontiguousarray(idx, dtype=np.int64))
+    return out

@@ -6,3 +6,4 @@ from .aqlm_oracle import (  # noqa: F401
     bits_per_weight, check_format, decode, decode_rows, forward, forward_rows,
     packed_bits_per_weight, product, within_tolerance,
 )
+from . import encoder_oracle  # noqa: F401
