@@ -168,3 +168,49 @@ def test_general_schemes_accepted(M, B, g):
         assert ENTRY[fn](s, FAKE, 0, FAKE) == 0
     # the same descriptor with a bad pointer is still rejected before any launch
     assert ENTRY["aqlm_gemv"](_layer(M=M, B=B, g=g, n_in=16 * g, codes=MISALIGNED), FAKE, 1, FAKE) == 4
+
+
+# ---------------------------------------------------------------------------
+# toy encoder entry points (include/aqlm_encode.h): exported, and validated on
+# the host before any launch
+# ---------------------------------------------------------------------------
+def test_encode_header_symbols_exported():
+    from additive_codebook_matmul_amd import encode as ENC
+    declared = _declared_functions(os.path.join(ROOT, "include", "aqlm_encode.h"))
+    assert declared == sorted(ENC.ENCODE_SYMBOLS)
+    lib = _lib.load_library()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_encode_validation():
+    from additive_codebook_matmul_amd import encode as ENC
+    lib = ENC._lib()
+    F, F2 = FAKE, FAKE + 0x100000
+    # normalize(W, out, in, scales, vecs)
+    assert lib.aqlm_encode_normalize(None, 4, 8, F, F2, None) == 1
+    assert lib.aqlm_encode_normalize(F, 0, 8, F, F2, None) == 2
+    assert lib.aqlm_encode_normalize(F, 4, 0, F, F2, None) == 2
+    assert lib.aqlm_encode_normalize(MISALIGNED, 4, 8, F, F2, None) == 4
+    # init(vecs, n, g, idx, K, cents)
+    assert lib.aqlm_encode_init(F, 10, 8, None, 256, F2, None) == 1
+    assert lib.aqlm_encode_init(F, 10, 12, F, 256, F2, None) == 3
+    assert lib.aqlm_encode_init(F, 10, 8, F, 300, F2, None) == 3
+    assert lib.aqlm_encode_init(F, 10, 8, F, 128, F2, None) == 3
+    assert lib.aqlm_encode_init(F, 0, 8, F, 256, F2, None) == 2
+    # assign(vecs, n, g, cents, K, codes, M, m, residual)
+    assert lib.aqlm_encode_assign(F, 0, 8, F2, 256, F, 2, 0, None, None) == 0   # n == 0: no-op
+    assert lib.aqlm_encode_assign(F, 10, 8, F2, 256, None, 2, 0, None, None) == 1
+    assert lib.aqlm_encode_assign(F, 10, 8, F2, 256, F, 2, 2, None, None) == 2  # m >= M
+    assert lib.aqlm_encode_assign(F, 10, 8, F2, 256, F, 9, 0, None, None) == 2
+    assert lib.aqlm_encode_assign(F, 10, 8, F2, 1 << 17, F, 2, 0, None, None) == 3
+    assert lib.aqlm_encode_assign(F, 10, 8, F2, 256, MISALIGNED, 2, 0, None, None) == 4
+    assert lib.aqlm_encode_assign(F, 10, 8, F2, 256, F, 2, 0, F + 16, None) == 2  # partial overlap
+    # update(vecs, n, g, codes, K, M, m, cents, ws)
+    assert lib.aqlm_encode_update(F, 10, 8, F, 256, 2, 0, F2, None, None) == 1
+    assert lib.aqlm_encode_update(F, 0, 8, F, 256, 2, 0, F2, F, None) == 2
+    assert lib.aqlm_encode_update(F, 10, 16, F, 256, 2, 0, F2, MISALIGNED, None) == 4
+    # round(cents, count, books, rounded)
+    assert lib.aqlm_encode_round(F, 0, F2, None, None) == 0
+    assert lib.aqlm_encode_round(None, 8, F2, None, None) == 1
+    assert lib.aqlm_encode_round(F, -1, F2, None, None) == 2
