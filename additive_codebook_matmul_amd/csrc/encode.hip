@@ -19,7 +19,7 @@ namespace aqlm {
 namespace {
 
 constexpr int kEncBlock = 256;
-constexpr int kAssignTileBytes = 64 * 1024;  // centroids staged in LDS per pass
+constexpr int kAssignTileBytes = 16 * 1024;  // centroids staged in LDS per pass
 constexpr float kFixedScale = 16777216.0f;   // 2^24
 constexpr double kFixedInv = 1.0 / 16777216.0;
 
@@ -63,8 +63,12 @@ __global__ __launch_bounds__(kEncBlock) void init_kernel(const float *__restrict
 
 // --- nearest centroid -------------------------------------------------------
 
-// One vector per thread, centroids streamed through LDS in tiles; every lane
+// Each thread owns kVPT vectors (independent dependency chains for the VALU,
+// and each centroid read from LDS serves all of them); centroids stream
+// through LDS in 16 KiB tiles so that eight workgroups fit on a CU. Every lane
 // of a wavefront reads the same centroid (a broadcast).
+constexpr int kVPT = 2;
+
 template <int G, typename CodeT>
 __global__ __launch_bounds__(kEncBlock) void assign_kernel(const float *__restrict__ vecs, int64_t n,
                                                            const float *__restrict__ cents, int K,
@@ -72,19 +76,28 @@ __global__ __launch_bounds__(kEncBlock) void assign_kernel(const float *__restri
                                                            float *residual) {
   constexpr int kTile = kAssignTileBytes / (G * 4);
   __shared__ __attribute__((aligned(16))) float tile[kTile * G];
-  const int64_t i = (int64_t)blockIdx.x * kEncBlock + threadIdx.x;
-  const bool live = i < n;
-  float v[G];
+  const int64_t i0 = ((int64_t)blockIdx.x * kEncBlock + threadIdx.x) * kVPT;
+  float v[kVPT][G];
 #pragma unroll
-  for (int u = 0; u < G / 4; ++u) {
-    const float4 t = live ? reinterpret_cast<const float4 *>(vecs + i * G)[u] : make_float4(0, 0, 0, 0);
-    v[4 * u] = t.x;
-    v[4 * u + 1] = t.y;
-    v[4 * u + 2] = t.z;
-    v[4 * u + 3] = t.w;
+  for (int p = 0; p < kVPT; ++p) {
+    const bool live = i0 + p < n;
+#pragma unroll
+    for (int u = 0; u < G / 4; ++u) {
+      const float4 t =
+          live ? reinterpret_cast<const float4 *>(vecs + (i0 + p) * G)[u] : make_float4(0, 0, 0, 0);
+      v[p][4 * u] = t.x;
+      v[p][4 * u + 1] = t.y;
+      v[p][4 * u + 2] = t.z;
+      v[p][4 * u + 3] = t.w;
+    }
   }
-  float best = __builtin_inff();
-  int bi = 0;
+  float best[kVPT];
+  int bi[kVPT];
+#pragma unroll
+  for (int p = 0; p < kVPT; ++p) {
+    best[p] = __builtin_inff();
+    bi[p] = 0;
+  }
   for (int c0 = 0; c0 < K; c0 += kTile) {
     const int nt = min(kTile, K - c0);
     __syncthreads();
@@ -93,25 +106,32 @@ __global__ __launch_bounds__(kEncBlock) void assign_kernel(const float *__restri
     __syncthreads();
     for (int c = 0; c < nt; ++c) {
       const float *cc = tile + c * G;
-      float t = v[0] - cc[0];
-      float d = t * t;
 #pragma unroll
-      for (int k = 1; k < G; ++k) {
-        t = v[k] - cc[k];
-        d = d + t * t;
-      }
-      if (d < best) {  // strict: the lowest code wins a tie
-        best = d;
-        bi = c0 + c;
+      for (int p = 0; p < kVPT; ++p) {
+        float t = v[p][0] - cc[0];
+        float d = t * t;
+#pragma unroll
+        for (int k = 1; k < G; ++k) {
+          t = v[p][k] - cc[k];
+          d = d + t * t;
+        }
+        if (d < best[p]) {  // strict: the lowest code wins a tie
+          best[p] = d;
+          bi[p] = c0 + c;
+        }
       }
     }
   }
-  if (!live) return;
-  codes[i * M + m] = (CodeT)bi;
-  if (residual) {
-    const float *cb = cents + (int64_t)bi * G;
 #pragma unroll
-    for (int k = 0; k < G; ++k) residual[i * G + k] = v[k] - cb[k];
+  for (int p = 0; p < kVPT; ++p) {
+    const int64_t i = i0 + p;
+    if (i >= n) break;
+    codes[i * M + m] = (CodeT)bi[p];
+    if (residual) {
+      const float *cb = cents + (int64_t)bi[p] * G;
+#pragma unroll
+      for (int k = 0; k < G; ++k) residual[i * G + k] = v[p][k] - cb[k];
+    }
   }
 }
 
@@ -190,7 +210,8 @@ unsigned grid_for(int64_t count) { return (unsigned)((count + kEncBlock - 1) / k
 template <int G, typename CodeT>
 hipError_t launch_assign_t(const float *vecs, int64_t n, const float *cents, int K, void *codes,
                            int M, int m, float *residual, hipStream_t stream) {
-  hipLaunchKernelGGL((assign_kernel<G, CodeT>), dim3(grid_for(n)), dim3(kEncBlock), 0, stream, vecs,
+  const int64_t threads = (n + kVPT - 1) / kVPT;
+  hipLaunchKernelGGL((assign_kernel<G, CodeT>), dim3(grid_for(threads)), dim3(kEncBlock), 0, stream, vecs,
                      n, cents, K, static_cast<CodeT *>(codes), M, m, residual);
   return hipGetLastError();
 }

@@ -56,7 +56,7 @@ def _parse():
     p.add_argument("--workload", default=WORKLOAD,
                    help="llama2_7b_2x8 (default: the headline step), or per-layer tables for "
                         "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, "
-                        "general_schemes, dequant")
+                        "general_schemes, dequant, or the toy encoder's kernels: encode")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device-to-device copies of MIB MiB (for scaling the HBM "
                         "byte counters of a profiler) and exit")
@@ -233,10 +233,73 @@ def per_layer_tables(args):
     return rows
 
 
+VALU_PEAK_TOPS = 78.6  # fp32 VALU ops/s: 157.3 TFLOP/s counts an FMA as two
+
+
+def encode_tables(args):
+    """Toy encoder kernels on a 4096 x 4096 dense float16 layer (2M group
+    vectors of 8): per-launch time of the nearest-codeword search for 256 and
+    65536 codewords (bound by VALU issue: 3g float32 operations per vector and
+    codeword, against 78.6 T operations/s), of the centroid update, and the
+    whole 2x8 encode with ten Lloyd iterations per codebook."""
+    import torch
+    from additive_codebook_matmul_amd import encode as ENC
+    from additive_codebook_matmul_amd import load_library
+    from additive_codebook_matmul_amd import workloads as WL
+    load_library()
+    dev = torch.device("cuda:0")
+    out = n_in = 4096
+    g = 8
+    n = out * n_in // g
+    W = torch.from_numpy(WL.make_dense_weight(out, n_in, seed=99)).to(dev)
+    scales, vecs = ENC.normalize(W)
+    v = vecs.view(n, g)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return 1e3 * t0.elapsed_time(t1) / reps
+
+    rows = []
+    for K, reps in ((256, 20), (65536, 2)):
+        idx = torch.from_numpy(WL.kmeans_init_indices(n, K, 1, seed=3)[0]).to(dev)
+        cents = torch.empty((K, g), dtype=torch.float32, device=dev)
+        ENC._check(ENC._lib().aqlm_encode_init(v.data_ptr(), n, g, idx.data_ptr(), K,
+                                               cents.data_ptr(), None))
+        codes = torch.empty((n, 1), dtype=torch.uint8 if K == 256 else torch.int16, device=dev)
+        us = timed(lambda: ENC.assign(v, cents, codes, 1, 0), reps)
+        ops = 3 * g * n * K
+        rows.append({"kernel": "aqlm_encode_assign", "vectors": n, "g": g, "K": K, "us": round(us, 1),
+                     "tops": round(ops / us / 1e6, 2),
+                     "pct_valu_peak": round(100 * ops / us / 1e6 / VALU_PEAK_TOPS, 1)})
+        ws = torch.empty(K * (g + 1), dtype=torch.int64, device=dev)
+        us = timed(lambda: ENC.update(v, codes, 1, 0, cents, ws), reps)
+        rows.append({"kernel": "aqlm_encode_update", "vectors": n, "g": g, "K": K, "us": round(us, 1),
+                     "gbps": round((n * g * 4 + n * codes.element_size()) / us / 1e3, 1)})
+    init = WL.kmeans_init_indices(n, 256, 2, seed=5)
+    t0 = time.perf_counter()
+    ENC.encode_layer(W, 2, 8, 8, 10, init)
+    torch.cuda.synchronize()
+    rows.append({"kernel": "encode_layer (2x8, 10 Lloyd iterations per codebook)", "out": out,
+                 "in": n_in, "ms": round(1e3 * (time.perf_counter() - t0), 1)})
+    for r in rows:
+        print(json.dumps({"workload": "encode", **r}), flush=True)
+    return rows
+
+
 def main():
     args = _parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload == "encode":
+        encode_tables(args)
         return
     if args.workload != WORKLOAD:
         per_layer_tables(args)
