@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "AQLM_OK", 1: "AQLM_ERR_NULL", 2: "AQLM_ERR_SHAPE", 3: "AQLM_
                 4: "AQLM_ERR_ALIGN", 5: "AQLM_ERR_BATCH", 6: "AQLM_ERR_HIP"}
 EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemv_batched", "aqlm_gemm",
                     "aqlm_status_string", "aqlm_abi_version")
-ABI_VERSION = 1
+ABI_VERSION = 2
+AQLM_CODES_PACKED = 1
 SCHEMES = {(2, 8, 8): "2x8", (1, 16, 8): "1x16", (1, 16, 16): "1x16g16"}
 
 
@@ -34,7 +35,7 @@ class AqlmLayerStruct(ctypes.Structure):
         ("num_codebooks", ctypes.c_int32),
         ("nbits", ctypes.c_int32),
         ("group_size", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("codes", ctypes.c_void_p),
         ("codebooks", ctypes.c_void_p),
         ("scales", ctypes.c_void_p),
@@ -101,24 +102,39 @@ def _stream_handle(device: torch.device) -> int:
 class AqlmLayer:
     """A quantized linear layer held as device tensors in the packed format.
 
-    codes      [out, in/g, M]  torch.uint8 (B = 8) or torch.int16/uint16 bits (B > 8)
+    codes      [out, in/g, M]  torch.uint8 (B = 8) or torch.int16/uint16 bits (B > 8),
+               or the bit-packed stream: a 1-D torch.int32/uint32 tensor of
+               ceil(out * in/g * M * B / 32) words (then in_features is required)
     codebooks  [M, 2**B, g]    torch.float16
     scales     [out]           torch.float16
     """
 
-    def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor):
-        if codes.dim() != 3 or codebooks.dim() != 3 or scales.dim() != 1:
-            raise ValueError("codes [out, in/g, M], codebooks [M, 2**B, g], scales [out]")
-        out, J, M = codes.shape
-        Mc, ncode, g = codebooks.shape
-        if Mc != M or scales.shape[0] != out:
-            raise ValueError("codes, codebooks and scales disagree in shape")
+    def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor,
+                 in_features: Optional[int] = None):
+        if codebooks.dim() != 3 or scales.dim() != 1 or codes.dim() not in (1, 3):
+            raise ValueError("codes [out, in/g, M] (or a packed 1-D stream), "
+                             "codebooks [M, 2**B, g], scales [out]")
+        M, ncode, g = codebooks.shape
+        out = scales.shape[0]
         if ncode < 2 or ncode & (ncode - 1):
             raise ValueError("codebook size must be a power of two")
         B = ncode.bit_length() - 1
-        want = (torch.uint8,) if B <= 8 else (torch.int16, torch.uint16)
-        if codes.dtype not in want:
-            raise ValueError(f"codes dtype {codes.dtype} does not match {B}-bit codes")
+        self.packed = codes.dim() == 1
+        if self.packed:
+            if in_features is None or in_features % g:
+                raise ValueError("a packed code stream needs in_features, a multiple of g")
+            J = in_features // g
+            if codes.dtype not in (torch.int32, torch.uint32):
+                raise ValueError("a packed code stream is 32-bit words")
+            if codes.numel() != (out * J * M * B + 31) // 32:
+                raise ValueError("packed code stream length does not match the layer")
+        else:
+            out_c, J, Mcodes = codes.shape
+            if Mcodes != M or out_c != out:
+                raise ValueError("codes, codebooks and scales disagree in shape")
+            want = (torch.uint8,) if B <= 8 else (torch.int16, torch.uint16)
+            if codes.dtype not in want:
+                raise ValueError(f"codes dtype {codes.dtype} does not match {B}-bit codes")
         if codebooks.dtype != torch.float16 or scales.dtype != torch.float16:
             raise ValueError("codebooks and scales must be float16")
         for t in (codes, codebooks, scales):
@@ -133,8 +149,8 @@ class AqlmLayer:
         self.M, self.B, self.g = int(M), int(B), int(g)
         self.device = codes.device
         self._struct = AqlmLayerStruct(self.out_features, self.in_features, self.M, self.B, self.g,
-                                       0, codes.data_ptr(), codebooks.data_ptr(),
-                                       scales.data_ptr())
+                                       AQLM_CODES_PACKED if self.packed else 0, codes.data_ptr(),
+                                       codebooks.data_ptr(), scales.data_ptr())
 
     @property
     def scheme(self) -> str:

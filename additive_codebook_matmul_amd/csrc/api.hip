@@ -27,11 +27,15 @@ int check_layer(const aqlm_layer *layer, aqlm::LayerDesc *d) {
     s = aqlm::Scheme::kGeneral;
   else
     return AQLM_ERR_SCHEME;
-  if (layer->reserved != 0) return AQLM_ERR_SHAPE;
+  if (layer->flags != 0 && layer->flags != AQLM_CODES_PACKED) return AQLM_ERR_SHAPE;
   if (layer->out_features < 1 || layer->in_features < 1) return AQLM_ERR_SHAPE;
   if (layer->in_features % g) return AQLM_ERR_SHAPE;
   // Kernels index rows and columns with 32-bit integers.
   if (layer->out_features > INT_MAX / 2 || layer->in_features > INT_MAX / 2) return AQLM_ERR_SHAPE;
+  // bit-packed streams are read with 32-bit byte offsets
+  const bool packed = layer->flags == AQLM_CODES_PACKED;
+  if (packed && layer->out_features * (layer->in_features / g) >= ((int64_t)1 << 35) / (M * B))
+    return AQLM_ERR_SHAPE;
   if (!aligned16(layer->codes) || !aligned16(layer->codebooks) || !aligned16(layer->scales))
     return AQLM_ERR_ALIGN;
   d->out = layer->out_features;
@@ -41,6 +45,7 @@ int check_layer(const aqlm_layer *layer, aqlm::LayerDesc *d) {
   d->M = M;
   d->B = B;
   d->g = g;
+  d->packed = packed;
   d->codes = layer->codes;
   d->books = layer->codebooks;
   d->scales = layer->scales;
@@ -60,7 +65,7 @@ const char *aqlm_status_string(int status) {
     case AQLM_OK: return "ok";
     case AQLM_ERR_NULL: return "a required pointer is NULL";
     case AQLM_ERR_SHAPE: return "invalid shape: need out >= 1, in >= 1, in % group_size == 0, "
-                                "sizes below 2^30 and reserved == 0";
+                                "sizes below 2^30 and flags 0 or AQLM_CODES_PACKED";
     case AQLM_ERR_SCHEME: return "unsupported scheme: need 1 <= M <= 8 codebooks, 8 <= B <= 16 "
                                  "code bits and group size 8 or 16";
     case AQLM_ERR_ALIGN: return "a pointer is not 16-byte aligned";

@@ -47,6 +47,9 @@ __device__ __forceinline__ uint2 buf_load8(Rsrc r, uint32_t off) {
   const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   return make_uint2(v.x, v.y);
 }
+__device__ __forceinline__ uint32_t buf_load4(Rsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 // 16-bit load zero-extended into its own 32-bit register (kept unpacked so a
 // refill never has to merge into a register another value lives in).
 __device__ __forceinline__ uint32_t buf_load_u16(Rsrc r, uint32_t off) {

@@ -20,7 +20,9 @@ struct LayerDesc {
   int64_t groups;        // in / g
   Scheme scheme;
   int M, B, g;           // codebooks, code bits, codeword length
-  const void *codes;     // [out][groups][M]; uint8 codes when B == 8, uint16 when B > 8
+  bool packed;           // codes bit-packed into 32-bit words (B bits each)
+  const void *codes;     // [out][groups][M]; uint8 codes when B == 8, uint16 when B > 8,
+                         // or the bit-packed stream
   const uint16_t *books; // [M][2^B][g] fp16 bits
   const uint16_t *scales;// [out] fp16 bits
 };

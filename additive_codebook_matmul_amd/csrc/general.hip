@@ -7,7 +7,8 @@
 // Language Models via Additive Quantization" summary, table "Measured effects
 // reported in the paper"). Codes are stored one per
 // element, in uint8 when B = 8 and in uint16 when B > 8, laid out
-// [out][in/g][M]; codebooks [M][2^B][g] fp16; one fp16 scale per output row.
+// [out][in/g][M], or bit-packed (B bits each, least significant first, in
+// 32-bit words); codebooks [M][2^B][g] fp16; one fp16 scale per output row.
 //
 // These kernels serve every scheme other than 2x8, 1x16 and 1x16 g16, which
 // have dedicated kernels. Each lane decodes whole groups exactly: the M
@@ -28,22 +29,44 @@ namespace {
 
 constexpr int kGenBlock = 256;
 
-// Code m of the group starting at p (CB bytes per code).
+// Where a layer's codes are: one per uint8 (CB = 1) or uint16 (CB = 2)
+// element, or bit-packed (CB = 0): B bits per code, least significant first,
+// in a stream of 32-bit words read through a buffer resource (a window past
+// the last word reads zero).
+struct Codes {
+  const uint8_t *p;
+  uint32_t bytes;  // of a bit-packed stream
+};
+
+__host__ __device__ inline uint32_t packed_stream_bytes(int64_t ncodes, int B) {
+  return (uint32_t)(((ncodes * B + 31) / 32) * 4);
+}
+
+// Code m of group gidx (the group's index in [out][in/g] order).
 template <int CB>
-__device__ __forceinline__ uint32_t code_at(const uint8_t *p, int m) {
-  if constexpr (CB == 1)
-    return p[m];
-  else
-    return reinterpret_cast<const uint16_t *>(p)[m];
+__device__ __forceinline__ uint32_t code_at(const Codes &c, int64_t gidx, int M, int B, int m) {
+  const int64_t i = gidx * M + m;
+  if constexpr (CB == 1) {
+    return c.p[i];
+  } else if constexpr (CB == 2) {
+    return reinterpret_cast<const uint16_t *>(c.p)[i];
+  } else {
+    const uint64_t bit = (uint64_t)i * (uint64_t)B;
+    const uint32_t word = (uint32_t)(bit >> 5), sh = (uint32_t)(bit & 31u);
+    const Rsrc rc = make_rsrc(c.p, c.bytes);
+    const uint64_t win = (uint64_t)buf_load4(rc, word * 4u) |
+                         ((uint64_t)buf_load4(rc, word * 4u + 4u) << 32);
+    return (uint32_t)(win >> sh) & ((1u << B) - 1u);
+  }
 }
 
 // Float32 sum of the group's M codewords in ascending m, starting from the
 // m = 0 codeword (so -0 + -0 stays -0).
 template <int G, int CB>
-__device__ __forceinline__ void group_sum(const uint8_t *cp, const uint4 *books, int M, int B,
-                                          float (&acc)[G]) {
+__device__ __forceinline__ void group_sum(const Codes &cs, int64_t gidx, const uint4 *books, int M,
+                                          int B, float (&acc)[G]) {
   {
-    const uint4 *cw = books + (size_t)code_at<CB>(cp, 0) * (G / 8);
+    const uint4 *cw = books + (size_t)code_at<CB>(cs, gidx, M, B, 0) * (G / 8);
 #pragma unroll
     for (int v = 0; v < G / 8; ++v) {
       const uint4 w = cw[v];
@@ -56,7 +79,7 @@ __device__ __forceinline__ void group_sum(const uint8_t *cp, const uint4 *books,
     }
   }
   for (int m = 1; m < M; ++m) {
-    const uint4 *cw = books + (((size_t)m << B) + code_at<CB>(cp, m)) * (G / 8);
+    const uint4 *cw = books + (((size_t)m << B) + code_at<CB>(cs, gidx, M, B, m)) * (G / 8);
 #pragma unroll
     for (int v = 0; v < G / 8; ++v) {
       const uint4 w = cw[v];
@@ -89,7 +112,7 @@ __device__ __forceinline__ void scale_round(const float (&acc)[G], float s, uint
 
 template <int G, int CB>
 __global__ __launch_bounds__(kGenBlock) void dequant_general_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
+    Codes codes, const uint16_t *__restrict__ books,
     const uint16_t *__restrict__ scales, uint16_t *__restrict__ W, int64_t groups, int64_t total,
     int M, int B) {
   const uint4 *gb = reinterpret_cast<const uint4 *>(books);
@@ -97,7 +120,7 @@ __global__ __launch_bounds__(kGenBlock) void dequant_general_kernel(
        idx += (int64_t)gridDim.x * kGenBlock) {
     const int64_t o = idx / groups;
     float acc[G];
-    group_sum<G, CB>(codes + idx * M * CB, gb, M, B, acc);
+    group_sum<G, CB>(codes, idx, gb, M, B, acc);
     uint4 w[G / 8];
     scale_round<G>(acc, h2f(scales[o]), w);
     // W[o][j*G ..] with idx = o * groups + j, and in = groups * G
@@ -111,22 +134,20 @@ __global__ __launch_bounds__(kGenBlock) void dequant_general_kernel(
 // groups l, l + 64, ... of the row.
 template <int G, int CB, int MAXB>
 __global__ __launch_bounds__(kGenBlock) void gemv_general_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
+    Codes codes, const uint16_t *__restrict__ books,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
     uint16_t *__restrict__ y, int out, int in, int groups, int batch, int M, int B) {
   const uint4 *gb = reinterpret_cast<const uint4 *>(books);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t row_bytes = (int64_t)groups * M * CB;
   for (int row = blockIdx.x * (kGenBlock / 64) + wave; row < out;
        row += gridDim.x * (kGenBlock / 64)) {
     float dot[MAXB];
 #pragma unroll
     for (int b = 0; b < MAXB; ++b) dot[b] = 0.0f;
-    const uint8_t *crow = codes + row * row_bytes;
     for (int j = lane; j < groups; j += 64) {
       float acc[G];
-      group_sum<G, CB>(crow + (int64_t)j * M * CB, gb, M, B, acc);
+      group_sum<G, CB>(codes, (int64_t)row * groups + j, gb, M, B, acc);
 #pragma unroll
       for (int b = 0; b < MAXB; ++b) {
         if (b < batch) {
@@ -163,7 +184,7 @@ constexpr int kGenLd = kGenTile + 8;  // padded LDS row (halves): conflict-free 
 
 template <int G, int CB>
 __global__ __launch_bounds__(kGenBlock) void gemm_general_kernel(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
+    Codes codes, const uint16_t *__restrict__ books,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x,
     uint16_t *__restrict__ y, int out, int in, int groups, int batch, int M, int B) {
   constexpr int GPT = kGenTile / G;  // groups per tile row
@@ -173,7 +194,6 @@ __global__ __launch_bounds__(kGenBlock) void gemm_general_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int row0 = blockIdx.x * kGenTile, tok0 = blockIdx.y * kGenTile;
-  const int64_t row_bytes = (int64_t)groups * M * CB;
   const int nk = (in + kGenTile - 1) / kGenTile;
 
   float16_t acc;
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(kGenBlock) void gemm_general_kernel(
       uint4 w[G / 8];
       if (row < out && j < groups) {
         float a[G];
-        group_sum<G, CB>(codes + row * row_bytes + (int64_t)j * M * CB, gb, M, B, a);
+        group_sum<G, CB>(codes, (int64_t)row * groups + j, gb, M, B, a);
         scale_round<G>(a, h2f(scales[row]), w);
       } else {
 #pragma unroll
@@ -229,6 +249,20 @@ __global__ __launch_bounds__(kGenBlock) void gemm_general_kernel(
   }
 }
 
+Codes codes_of(const LayerDesc &L) {
+  const uint8_t *p = static_cast<const uint8_t *>(L.codes);
+  const uint32_t bytes = L.packed ? packed_stream_bytes(L.out * L.groups * L.M, L.B) : 0u;
+  return Codes{p, bytes};
+}
+
+// Bytes per stored code: 1 (B = 8), 2 (B > 8), or 0 for a bit-packed stream
+// of B < 16 bits (for B = 8 and 16 the stream is the element layout).
+int code_bytes(const LayerDesc &L) {
+  if (L.B == 8) return 1;
+  if (L.B == 16 || !L.packed) return 2;
+  return 0;
+}
+
 int grid_cap(int64_t n, int per_block) {
   const int64_t blocks = (n + per_block - 1) / per_block;
   return (int)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
@@ -238,8 +272,8 @@ template <int G, int CB>
 hipError_t dequant_gc(const LayerDesc &L, uint16_t *W, hipStream_t stream) {
   const int64_t total = L.out * L.groups;
   hipLaunchKernelGGL((dequant_general_kernel<G, CB>), dim3(grid_cap(total, kGenBlock)),
-                     dim3(kGenBlock), 0, stream, static_cast<const uint8_t *>(L.codes), L.books,
-                     L.scales, W, L.groups, total, L.M, L.B);
+                     dim3(kGenBlock), 0, stream, codes_of(L), L.books, L.scales, W, L.groups,
+                     total, L.M, L.B);
   return hipGetLastError();
 }
 
@@ -248,8 +282,8 @@ hipError_t gemv_gc(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y
                    hipStream_t stream) {
   hipLaunchKernelGGL((gemv_general_kernel<G, CB, MAXB>),
                      dim3(grid_cap(L.out, kGenBlock / 64)), dim3(kGenBlock), 0, stream,
-                     static_cast<const uint8_t *>(L.codes), L.books, L.scales, x, y, (int)L.out,
-                     (int)L.in, (int)L.groups, batch, L.M, L.B);
+                     codes_of(L), L.books, L.scales, x, y, (int)L.out, (int)L.in, (int)L.groups,
+                     batch, L.M, L.B);
   return hipGetLastError();
 }
 
@@ -268,33 +302,44 @@ hipError_t gemm_gc(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_
   const dim3 grid((unsigned)((L.out + kGenTile - 1) / kGenTile),
                   (unsigned)((batch + kGenTile - 1) / kGenTile));
   hipLaunchKernelGGL((gemm_general_kernel<G, CB>), grid, dim3(kGenBlock), 0, stream,
-                     static_cast<const uint8_t *>(L.codes), L.books, L.scales, x, y, (int)L.out,
-                     (int)L.in, (int)L.groups, (int)batch, L.M, L.B);
+                     codes_of(L), L.books, L.scales, x, y, (int)L.out, (int)L.in, (int)L.groups,
+                     (int)batch, L.M, L.B);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_dequant_general(const LayerDesc &L, uint16_t *W, hipStream_t stream) {
-  const bool wide = L.B > 8;
-  if (L.g == 8) return wide ? dequant_gc<8, 2>(L, W, stream) : dequant_gc<8, 1>(L, W, stream);
-  return wide ? dequant_gc<16, 2>(L, W, stream) : dequant_gc<16, 1>(L, W, stream);
+  const int cb = code_bytes(L);
+  if (L.g == 8)
+    return cb == 1 ? dequant_gc<8, 1>(L, W, stream)
+                   : (cb == 2 ? dequant_gc<8, 2>(L, W, stream) : dequant_gc<8, 0>(L, W, stream));
+  return cb == 1 ? dequant_gc<16, 1>(L, W, stream)
+                 : (cb == 2 ? dequant_gc<16, 2>(L, W, stream) : dequant_gc<16, 0>(L, W, stream));
 }
 
 hipError_t launch_gemv_general(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
                                hipStream_t stream) {
-  const bool wide = L.B > 8;
+  const int cb = code_bytes(L);
   if (L.g == 8)
-    return wide ? gemv_g<8, 2>(L, x, batch, y, stream) : gemv_g<8, 1>(L, x, batch, y, stream);
-  return wide ? gemv_g<16, 2>(L, x, batch, y, stream) : gemv_g<16, 1>(L, x, batch, y, stream);
+    return cb == 1 ? gemv_g<8, 1>(L, x, batch, y, stream)
+                   : (cb == 2 ? gemv_g<8, 2>(L, x, batch, y, stream)
+                              : gemv_g<8, 0>(L, x, batch, y, stream));
+  return cb == 1 ? gemv_g<16, 1>(L, x, batch, y, stream)
+                 : (cb == 2 ? gemv_g<16, 2>(L, x, batch, y, stream)
+                            : gemv_g<16, 0>(L, x, batch, y, stream));
 }
 
 hipError_t launch_gemm_general(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                                hipStream_t stream) {
-  const bool wide = L.B > 8;
+  const int cb = code_bytes(L);
   if (L.g == 8)
-    return wide ? gemm_gc<8, 2>(L, x, batch, y, stream) : gemm_gc<8, 1>(L, x, batch, y, stream);
-  return wide ? gemm_gc<16, 2>(L, x, batch, y, stream) : gemm_gc<16, 1>(L, x, batch, y, stream);
+    return cb == 1 ? gemm_gc<8, 1>(L, x, batch, y, stream)
+                   : (cb == 2 ? gemm_gc<8, 2>(L, x, batch, y, stream)
+                              : gemm_gc<8, 0>(L, x, batch, y, stream));
+  return cb == 1 ? gemm_gc<16, 1>(L, x, batch, y, stream)
+                 : (cb == 2 ? gemm_gc<16, 2>(L, x, batch, y, stream)
+                            : gemm_gc<16, 0>(L, x, batch, y, stream));
 }
 
 }  // namespace aqlm

@@ -28,6 +28,8 @@ namespace {
 struct HostLayer {
   int64_t out, in, groups;
   int M, B, g;
+  bool packed;       // B-bit codes in 32-bit words, least significant first
+  int64_t nwords;    // words of a packed stream
   const void *codes;
   const uint16_t *books;
   const uint16_t *scales;
@@ -38,7 +40,7 @@ int check_layer(const aqlm_layer *layer, HostLayer *d) {
   if (!layer->codes || !layer->codebooks || !layer->scales) return AQLM_ERR_NULL;
   const int M = layer->num_codebooks, B = layer->nbits, g = layer->group_size;
   if (!(M >= 1 && M <= 8 && B >= 8 && B <= 16 && (g == 8 || g == 16))) return AQLM_ERR_SCHEME;
-  if (layer->reserved != 0) return AQLM_ERR_SHAPE;
+  if (layer->flags != 0 && layer->flags != AQLM_CODES_PACKED) return AQLM_ERR_SHAPE;
   if (layer->out_features < 1 || layer->in_features < 1) return AQLM_ERR_SHAPE;
   if (layer->in_features % g) return AQLM_ERR_SHAPE;
   if (layer->out_features > (int64_t(1) << 30) || layer->in_features > (int64_t(1) << 30))
@@ -49,6 +51,8 @@ int check_layer(const aqlm_layer *layer, HostLayer *d) {
   d->M = M;
   d->B = B;
   d->g = g;
+  d->packed = layer->flags == AQLM_CODES_PACKED && B != 8 && B != 16;
+  d->nwords = (d->out * d->groups * M * B + 31) / 32;
   d->codes = layer->codes;
   d->books = layer->codebooks;
   d->scales = layer->scales;
@@ -101,6 +105,13 @@ inline uint16_t float_to_half(float f) {
 
 inline uint32_t code_at(const HostLayer &L, int64_t o, int64_t j, int m) {
   const int64_t i = (o * L.groups + j) * L.M + m;
+  if (L.packed) {
+    const uint32_t *w = static_cast<const uint32_t *>(L.codes);
+    const uint64_t bit = (uint64_t)i * (uint64_t)L.B;
+    const int64_t k = (int64_t)(bit >> 5);
+    const uint64_t win = (uint64_t)w[k] | (k + 1 < L.nwords ? (uint64_t)w[k + 1] << 32 : 0);
+    return (uint32_t)(win >> (bit & 31)) & ((1u << L.B) - 1u);
+  }
   return L.B == 8 ? static_cast<const uint8_t *>(L.codes)[i]
                   : static_cast<const uint16_t *>(L.codes)[i];
 }

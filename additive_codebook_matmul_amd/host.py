@@ -14,7 +14,7 @@ from typing import Optional
 
 import numpy as np
 
-from ._lib import AQLM_OK, STATUS_NAMES, AqlmError, AqlmLayerStruct
+from ._lib import AQLM_CODES_PACKED, AQLM_OK, STATUS_NAMES, AqlmError, AqlmLayerStruct
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 HOST_LIB_PATH = os.path.join(_PKG_DIR, "libaqlm_host.so")
@@ -49,22 +49,33 @@ def host_gemv(codes: np.ndarray, codebooks: np.ndarray, scales: np.ndarray, x: n
               threads: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
     """y = x . W^T on the host for 1..8 activation rows (aqlm_host_gemv).
 
-    codes [out, in/g, M] uint8 (B = 8) or uint16 (B > 8); codebooks [M, 2**B, g]
-    float16; scales [out] float16; x [batch, in] float16. Returns [batch, out]
-    float16. threads <= 0 lets the OpenMP runtime choose.
+    codes [out, in/g, M] uint8 (B = 8) or uint16 (B > 8), or the bit-packed
+    stream as a 1-D uint32 array; codebooks [M, 2**B, g] float16; scales [out]
+    float16; x [batch, in] float16. Returns [batch, out] float16. threads <= 0
+    lets the OpenMP runtime choose.
     """
     lib = load_host_library()
-    if codes.ndim != 3 or codebooks.ndim != 3 or scales.ndim != 1 or x.ndim != 2:
-        raise ValueError("codes [out, in/g, M], codebooks [M, 2**B, g], scales [out], x [batch, in]")
-    n_out, J, M = codes.shape
+    if codes.ndim not in (1, 3) or codebooks.ndim != 3 or scales.ndim != 1 or x.ndim != 2:
+        raise ValueError("codes [out, in/g, M] or a packed stream, codebooks [M, 2**B, g], "
+                         "scales [out], x [batch, in]")
     Mc, ncode, g = codebooks.shape
-    if Mc != M or scales.shape[0] != n_out:
-        raise ValueError("codes, codebooks and scales disagree in shape")
     if ncode < 2 or ncode & (ncode - 1):
         raise ValueError("codebook size must be a power of two")
     B = ncode.bit_length() - 1
-    if codes.dtype != (np.uint8 if B <= 8 else np.uint16):
-        raise ValueError(f"codes dtype {codes.dtype} does not match {B}-bit codes")
+    M, n_out = Mc, scales.shape[0]
+    packed = codes.ndim == 1
+    if packed:
+        if x.shape[1] % g:
+            raise ValueError("in must be a multiple of g")
+        J = x.shape[1] // g
+        if codes.dtype != np.uint32 or codes.size != (n_out * J * M * B + 31) // 32:
+            raise ValueError("a packed code stream is ceil(out*in/g*M*B/32) uint32 words")
+    else:
+        n_out_c, J, Mcodes = codes.shape
+        if Mcodes != M or n_out_c != n_out:
+            raise ValueError("codes, codebooks and scales disagree in shape")
+        if codes.dtype != (np.uint8 if B <= 8 else np.uint16):
+            raise ValueError(f"codes dtype {codes.dtype} does not match {B}-bit codes")
     for a, name in ((codebooks, "codebooks"), (scales, "scales"), (x, "x")):
         if a.dtype != np.float16:
             raise ValueError(f"{name} must be float16")
@@ -77,7 +88,8 @@ def host_gemv(codes: np.ndarray, codebooks: np.ndarray, scales: np.ndarray, x: n
         out = np.empty((batch, n_out), dtype=np.float16)
     elif out.shape != (batch, n_out) or out.dtype != np.float16 or not out.flags.c_contiguous:
         raise ValueError("out must be a contiguous float16 [batch, out] array")
-    st = AqlmLayerStruct(int(n_out), int(J * g), int(M), int(B), int(g), 0,
+    st = AqlmLayerStruct(int(n_out), int(J * g), int(M), int(B), int(g),
+                         AQLM_CODES_PACKED if packed else 0,
                          codes.ctypes.data, codebooks.ctypes.data, scales.ctypes.data)
     status = lib.aqlm_host_gemv(ctypes.byref(st), x.ctypes.data, batch, out.ctypes.data,
                                 int(threads))

@@ -59,6 +59,7 @@ class Layer:
     in_features: int
     scheme: Scheme
     seed: int
+    packed: bool = False  # codes handed over bit-packed (pack_codes) rather than one per element
 
 
 @dataclass(frozen=True)
@@ -100,9 +101,18 @@ GENERAL_SCHEMES = (Scheme(1, 8, 8), Scheme(3, 8, 8), Scheme(4, 8, 8), Scheme(4, 
                    Scheme(8, 8, 16), Scheme(1, 12, 8), Scheme(2, 12, 16), Scheme(2, 16, 8))
 
 
+# The same, with codes bit-packed: B bits per code whatever B is, so that the
+# codes cost exactly M*B/g bits per weight.
+PACKED_SCHEMES = (Scheme(1, 12, 8), Scheme(2, 12, 16), Scheme(2, 10, 8), Scheme(3, 9, 16))
+
+
 def _general_layers(index: int) -> Tuple[Layer, ...]:
-    return tuple(Layer(f"q_{s.name}", 4096, 4096, s, 1000 * index + li)
-                 for li, s in enumerate(GENERAL_SCHEMES))
+    plain = tuple(Layer(f"q_{s.name}", 4096, 4096, s, 1000 * index + li)
+                  for li, s in enumerate(GENERAL_SCHEMES))
+    base = len(plain)
+    packed = tuple(Layer(f"q_{s.name}_packed", 4096, 4096, s, 1000 * index + base + li, True)
+                   for li, s in enumerate(PACKED_SCHEMES))
+    return plain + packed
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -181,11 +191,30 @@ def small_case(out_features: int, in_features: int, scheme: Scheme, batch: int,
     return codes, codebooks, scales, x
 
 
+def pack_codes(codes: np.ndarray, B: int) -> np.ndarray:
+    """The bit-packed storage of a code array: code i of the flattened array
+    occupies bits i*B .. i*B+B-1 of a stream of little-endian 32-bit words,
+    least significant bit first. Returns ceil(n*B/32) uint32 words."""
+    flat = np.asarray(codes).reshape(-1).astype(np.uint64)
+    nwords = (flat.size * B + 31) // 32
+    words = np.zeros(nwords + 1, dtype=np.uint64)
+    bit = np.arange(flat.size, dtype=np.uint64) * np.uint64(B)
+    word = (bit >> np.uint64(5)).astype(np.int64)
+    shifted = flat << (bit & np.uint64(31))
+    # codes occupy disjoint bits, so adding them into a word never carries
+    np.add.at(words, word, shifted & np.uint64(0xFFFFFFFF))
+    np.add.at(words, word + 1, shifted >> np.uint64(32))
+    return words[:nwords].astype(np.uint32)
+
+
 def workload_bytes(layer: Layer, batch: int) -> Dict[str, int]:
     """Byte counts of the packed tensors and activations of one layer."""
     s = layer.scheme
     J = layer.in_features // s.g
-    code_bytes = layer.out_features * J * s.M * np.dtype(s.code_dtype).itemsize
+    if layer.packed:
+        code_bytes = (layer.out_features * J * s.M * s.B + 31) // 32 * 4
+    else:
+        code_bytes = layer.out_features * J * s.M * np.dtype(s.code_dtype).itemsize
     return {
         "codes": code_bytes,
         "codebooks": s.M * (2 ** s.B) * s.g * 2,

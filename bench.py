@@ -195,16 +195,21 @@ def per_layer_tables(args):
     rows = []
     for layer in wl.layers:
         d = WL.make_layer(layer)
-        codes = torch.from_numpy(d.codes.view("int16") if d.codes.dtype.name == "uint16" else d.codes).to(dev)
+        if layer.packed:
+            codes = torch.from_numpy(WL.pack_codes(d.codes, layer.scheme.B).view("int32")).to(dev)
+        else:
+            codes = torch.from_numpy(d.codes.view("int16") if d.codes.dtype.name == "uint16"
+                                     else d.codes).to(dev)
         books = torch.from_numpy(d.codebooks).to(dev)
         scales = torch.from_numpy(d.scales).to(dev)
+        kw = {"in_features": layer.in_features} if layer.packed else {}
         batches = (1,) if name == "dequant" else wl.batches
         for batch in batches:
             b = WL.workload_bytes(layer, batch)
             copies = max(2, min(64, -(-ROTATE_BYTES // b["codes"])))
             if batch > 8:
                 copies = max(2, min(copies, 8))
-            Ls = [AqlmLayer(codes.clone(), books, scales) for _ in range(copies)]
+            Ls = [AqlmLayer(codes.clone(), books, scales, **kw) for _ in range(copies)]
             x = torch.from_numpy(WL.make_x(layer, batch)).to(dev)
             op = "dequant" if name == "dequant" else ("gemm" if batch > 8 else "gemv")
             if op == "dequant":
@@ -219,7 +224,8 @@ def per_layer_tables(args):
             reps = max(2, 200 // copies)
             us = 1e3 * _time_graph(torch, g, reps) / copies
             row = {"layer": layer.name, "out": layer.out_features, "in": layer.in_features,
-                   "scheme": layer.scheme.name, "batch": batch, "us": round(us, 3),
+                   "scheme": layer.scheme.name, "packed_codes": layer.packed, "batch": batch,
+                   "us": round(us, 3),
                    "hbm_gbps": round(nbytes / us / 1e3, 1),
                    "pct_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBPS, 2)}
             if op == "gemm":

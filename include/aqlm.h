@@ -12,10 +12,17 @@
  *
  * Packed format (all arrays dense, row-major, little-endian):
  *   codes      [out][in/g][M]   uint8 when B == 8, uint16 when B > 8 (one
- *                               code per element, no bit packing); an
- *                               entry is an unsigned codeword index < 2^B
+ *                               code per element); an entry is an unsigned
+ *                               codeword index < 2^B
  *   codebooks  [M][2^B][g]      float16 bit patterns
  *   scales     [out]            float16 bit patterns, one per output row
+ * Bit-packed codes (flags = AQLM_CODES_PACKED): codes is instead a stream of
+ * ceil(out * (in/g) * M * B / 32) little-endian 32-bit words, and code m of
+ * group j of row o occupies bits p .. p + B - 1 of the stream, with
+ * p = ((o * (in/g) + j) * M + m) * B and bit p being bit p % 32 of word
+ * p / 32 (least significant first). The codes then cost exactly M * B / g
+ * bits per weight for every B; for B = 8 and B = 16 the stream holds the
+ * same bytes as the uint8 / uint16 arrays above.
  * Group j of output row o covers input columns j*g .. j*g+g-1, and
  *   W[o][j*g+k] = fp16_rne( float(scales[o]) *
  *                           (float(C_0[c_0][k]) + ... + float(C_{M-1}[c_{M-1}][k])) )
@@ -60,7 +67,10 @@
 extern "C" {
 #endif
 
-#define AQLM_ABI_VERSION 1
+#define AQLM_ABI_VERSION 2
+
+/* aqlm_layer.flags: codes are bit-packed (see the format above). */
+#define AQLM_CODES_PACKED 1
 
 #if defined(__GNUC__) || defined(__clang__)
 #define AQLM_API __attribute__((visibility("default")))
@@ -71,7 +81,8 @@ extern "C" {
 typedef enum aqlm_status {
   AQLM_OK = 0,
   AQLM_ERR_NULL = 1,   /* a required pointer is NULL */
-  AQLM_ERR_SHAPE = 2,  /* out < 1, in < 1, in % g != 0, or a size overflows */
+  AQLM_ERR_SHAPE = 2,  /* out < 1, in < 1, in % g != 0, a size overflows, or
+                          unknown flags */
   AQLM_ERR_SCHEME = 3, /* (M, B, g) is not a supported scheme */
   AQLM_ERR_ALIGN = 4,  /* a pointer is not 16-byte aligned */
   AQLM_ERR_BATCH = 5,  /* batch outside the entry point's range */
@@ -85,8 +96,9 @@ typedef struct aqlm_layer {
   int32_t num_codebooks;     /* M */
   int32_t nbits;             /* B: codebook size is 2^B */
   int32_t group_size;        /* g: codeword length */
-  int32_t reserved;          /* must be 0 */
-  const void *codes;         /* device, [out][in/g][M] uint8 (B=8) / uint16 (B>8) */
+  int32_t flags;             /* 0 or AQLM_CODES_PACKED */
+  const void *codes;         /* device, [out][in/g][M] uint8 (B=8) / uint16 (B>8),
+                                or the bit-packed word stream */
   const uint16_t *codebooks; /* device, [M][2^B][g] float16 bits */
   const uint16_t *scales;    /* device, [out] float16 bits */
 } aqlm_layer;

@@ -37,8 +37,9 @@ extern "C" {
 /*
  * aqlm_host_gemv: y[b][o] = sum_i x[b][i] * W[o][i] for b < batch,
  * 1 <= batch <= 8 (batch == 0 is a no-op returning AQLM_OK).
- *   layer    the packed layer as in aqlm.h, except that codes, codebooks and
- *            scales are HOST pointers (no alignment requirement)
+ *   layer    the packed layer as in aqlm.h (element or bit-packed codes),
+ *            except that codes, codebooks and scales are HOST pointers (no
+ *            alignment requirement)
  *   x        host, [batch][in] float16 bits
  *   y        host, [batch][out] float16 bits, written in full
  *   threads  worker threads (OpenMP); <= 0 uses the runtime's default

@@ -50,8 +50,25 @@ import numpy as np
 __all__ = [
     "check_format", "decode", "decode_rows", "product", "forward",
     "forward_rows", "within_tolerance", "bits_per_weight", "stored_bits_per_weight",
-    "packed_bits_per_weight",
+    "packed_bits_per_weight", "unpack_codes",
 ]
+
+
+def unpack_codes(words, out, J, M, B):
+    """Codes [out, J, M] from their bit-packed storage: code i of the flattened
+    array is bits i*B .. i*B+B-1 of the little-endian 32-bit word stream,
+    least significant bit first (the library's reading of a packed format the
+    pages leave unstated)."""
+    w = np.asarray(words, dtype=np.uint32).astype(np.uint64)
+    n = out * J * M
+    if w.size * 32 < n * B:
+        raise ValueError("packed stream too short")
+    bit = np.arange(n, dtype=np.uint64) * np.uint64(B)
+    k = (bit >> np.uint64(5)).astype(np.int64)
+    nxt = np.where(k + 1 < w.size, w[np.minimum(k + 1, w.size - 1)], np.uint64(0))
+    win = w[k] | (nxt << np.uint64(32))
+    codes = (win >> (bit & np.uint64(31))) & np.uint64((1 << B) - 1)
+    return codes.astype(np.uint8 if B == 8 else np.uint16).reshape(out, J, M)
 
 
 def check_format(codes, codebooks, scales):

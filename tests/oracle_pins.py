@@ -288,8 +288,27 @@ def pin_bits_per_weight(impl):
     assert round(bits / n, 2) == 2.07
 
 
+def pin_unpack_codes(impl):
+    """Bit-packed codes: a hand-packed stream, an independent bit-by-bit
+    reader, and the byte / halfword layouts that B = 8 and 16 must reproduce."""
+    got = impl.unpack_codes(np.array([0xFF123ABC, 0x0000000F], dtype=np.uint32), 1, 1, 3, 12)
+    assert got.tolist() == [[[0xABC, 0x123, 0xFFF]]]
+    rng = np.random.default_rng(21)
+    for B in (9, 10, 11, 12, 13, 15):
+        out, J, M = 5, 7, 3
+        n = out * J * M
+        words = rng.integers(0, 2 ** 32, size=(n * B + 31) // 32, dtype=np.uint64).astype(np.uint32)
+        bits = [(int(words[p // 32]) >> (p % 32)) & 1 for p in range(n * B)]
+        want = [sum(bits[i * B + t] << t for t in range(B)) for i in range(n)]
+        assert impl.unpack_codes(words, out, J, M, B).reshape(-1).tolist() == want
+    c8 = rng.integers(0, 256, size=(3, 4, 2), dtype=np.uint8)
+    assert np.array_equal(impl.unpack_codes(c8.reshape(-1).view(np.uint32), 3, 4, 2, 8), c8)
+    c16 = rng.integers(0, 65536, size=(3, 4, 2), dtype=np.uint16)
+    assert np.array_equal(impl.unpack_codes(c16.reshape(-1).view(np.uint32), 3, 4, 2, 16), c16)
+
+
 ALL_PINS = [
     pin_hand_worked, pin_rounding_cases, pin_brute_force_decode, pin_brute_force_product,
     pin_scalar_lut_special_case, pin_constant_codes, pin_zero_second_codebook,
-    pin_one_hot_columns, pin_linearity, pin_bits_per_weight,
+    pin_one_hot_columns, pin_linearity, pin_bits_per_weight, pin_unpack_codes,
 ]

@@ -57,8 +57,8 @@ def test_status_strings():
     assert _lib.status_string(0) == "ok"
 
 
-def _layer(M=2, B=8, g=8, out=64, n_in=128, codes=FAKE, books=FAKE, scales=FAKE, reserved=0):
-    return _lib.AqlmLayerStruct(out, n_in, M, B, g, reserved, codes, books, scales)
+def _layer(M=2, B=8, g=8, out=64, n_in=128, codes=FAKE, books=FAKE, scales=FAKE, flags=0):
+    return _lib.AqlmLayerStruct(out, n_in, M, B, g, flags, codes, books, scales)
 
 
 ENTRY = {
@@ -84,7 +84,7 @@ def test_null_layer_pointer(fn):
     (dict(M=0), 3), (dict(M=9), 3), (dict(B=7), 3), (dict(B=17), 3), (dict(g=4), 3),
     (dict(g=32), 3), (dict(M=-1), 3),
     (dict(out=0), 2), (dict(n_in=0), 2), (dict(n_in=100), 2), (dict(out=-5), 2),
-    (dict(reserved=1), 2), (dict(out=1 << 40), 2),
+    (dict(flags=2), 2), (dict(flags=-1), 2), (dict(out=1 << 40), 2),
     (dict(M=1, B=16, g=16, n_in=136), 2),
     (dict(codes=MISALIGNED), 4), (dict(books=MISALIGNED), 4), (dict(scales=MISALIGNED), 4),
 ])

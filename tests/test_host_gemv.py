@@ -63,6 +63,20 @@ def test_host_small(scheme, out, J, isa):
         _check(y, y_ref, bound, f"{scheme.name} {out}x{J} b{batch} {isa}")
 
 
+@pytest.mark.parametrize("scheme", [S(1, 12, 8), S(2, 10, 16), S(3, 9, 8), S(2, 8, 8), S(1, 16, 8)],
+                         ids=lambda s: s.name)
+def test_host_packed_codes(scheme, isa):
+    """Bit-packed code streams, unpacked on the oracle's side by its own reader."""
+    codes, books, scales, x = WL.small_case(65, 9 * scheme.g, scheme, 8, seed=13)
+    words = WL.pack_codes(codes, scheme.B)
+    unpacked = oracle.unpack_codes(words, 65, 9, scheme.M, scheme.B)
+    w = oracle.decode(unpacked, books, scales)
+    for batch in (1, 8):
+        y = host.host_gemv(words, books, scales, x[:batch], threads=2)
+        y_ref, bound = oracle.product(x[:batch], w)
+        _check(y, y_ref, bound, f"packed {scheme.name} b{batch} {isa}")
+
+
 @pytest.mark.parametrize("scheme", [S(2, 8, 8), S(1, 16, 8), S(3, 10, 16)], ids=lambda s: s.name)
 def test_host_threads_do_not_change_bits(scheme):
     codes, books, scales, x = WL.small_case(300, 40 * scheme.g, scheme, 8, seed=5)
@@ -124,8 +138,8 @@ def test_host_errors():
     codes, books, scales, x = WL.small_case(4, 16, S(2, 8, 8), 2, seed=1)
     y = np.empty((2, 4), dtype=np.float16)
 
-    def st(M=2, B=8, g=8, out=4, n_in=16, reserved=0, codes_p=codes.ctypes.data):
-        return AqlmLayerStruct(out, n_in, M, B, g, reserved, codes_p, books.ctypes.data,
+    def st(M=2, B=8, g=8, out=4, n_in=16, flags=0, codes_p=codes.ctypes.data):
+        return AqlmLayerStruct(out, n_in, M, B, g, flags, codes_p, books.ctypes.data,
                                scales.ctypes.data)
     xp, yp = x.ctypes.data, y.ctypes.data
     assert _call_raw(st(), xp, 2, yp) == 0
@@ -135,7 +149,7 @@ def test_host_errors():
     assert _call_raw(st(), None, 2, yp) == 1               # NULL x
     assert _call_raw(st(n_in=12), xp, 2, yp) == 2          # in % g
     assert _call_raw(st(out=0), xp, 2, yp) == 2
-    assert _call_raw(st(reserved=1), xp, 2, yp) == 2
+    assert _call_raw(st(flags=2), xp, 2, yp) == 2
     for M, B, g in ((0, 8, 8), (9, 8, 8), (2, 7, 8), (2, 17, 8), (2, 8, 4), (2, 8, 32)):
         assert _call_raw(st(M, B, g), xp, 2, yp) == 3
     assert _call_raw(st(), xp, 9, yp) == 5

@@ -19,7 +19,7 @@ def test_oracle_pin(pin):
 # Planted mistakes: each copy of the oracle below carries one plausible error;
 # the pin suite must reject every one of them.
 # ---------------------------------------------------------------------------
-def _impl(decode_rows=None, product=None):
+def _impl(decode_rows=None, product=None, unpack=None):
     ns = types.SimpleNamespace()
     dr = decode_rows or O.decode_rows
     pr = product or O.product
@@ -33,6 +33,7 @@ def _impl(decode_rows=None, product=None):
     ns.decode_rows, ns.decode, ns.forward, ns.product = dr, decode, forward, pr
     ns.bits_per_weight, ns.packed_bits_per_weight = O.bits_per_weight, O.packed_bits_per_weight
     ns.stored_bits_per_weight = O.stored_bits_per_weight
+    ns.unpack_codes = unpack or O.unpack_codes
     return ns
 
 
@@ -181,6 +182,26 @@ def p_fp32_accumulate_in_fp16(x, w16):
     return y.astype(np.float64), b
 
 
+def u_msb_first(words, out, J, M, B):
+    w = np.asarray(words, dtype=np.uint32)
+    bits = np.unpackbits(w.view(np.uint8), bitorder="big")
+    n = out * J * M
+    codes = [int("".join(str(b) for b in bits[i * B:(i + 1) * B]), 2) for i in range(n)]
+    return np.array(codes, dtype=np.uint8 if B == 8 else np.uint16).reshape(out, J, M)
+
+
+def u_byte_aligned(words, out, J, M, B):
+    # each code padded to whole bytes: the unpacked element layout read from the stream
+    w = np.asarray(words, dtype=np.uint32).view(np.uint8)
+    step = (B + 7) // 8
+    n = out * J * M
+    raw = np.zeros(n * step, dtype=np.uint8)
+    raw[:min(n * step, w.size)] = w[:n * step]
+    vals = raw.reshape(n, step).astype(np.uint32)
+    codes = vals[:, 0] | (vals[:, 1] << 8 if step > 1 else 0)
+    return (codes & ((1 << B) - 1)).astype(np.uint8 if B == 8 else np.uint16).reshape(out, J, M)
+
+
 MUTANTS = {
     "swapped_codebooks": _impl(decode_rows=m_swapped_codebooks),
     "fp16_sum_then_scale": _impl(decode_rows=m_fp16_sum_then_scale),
@@ -197,6 +218,8 @@ MUTANTS = {
     "product_drops_last_column": _impl(product=p_drop_last_column),
     "product_rows_reversed": _impl(product=p_transposed_rows),
     "product_accumulates_in_fp16": _impl(product=p_fp32_accumulate_in_fp16),
+    "packed_codes_msb_first": _impl(unpack=u_msb_first),
+    "packed_codes_byte_aligned": _impl(unpack=u_byte_aligned),
 }
 
 
