@@ -19,10 +19,12 @@ LIB_PATH = os.path.join(_PKG_DIR, "libaqlm_mi355x.so")
 
 AQLM_OK = 0
 STATUS_NAMES = {0: "AQLM_OK", 1: "AQLM_ERR_NULL", 2: "AQLM_ERR_SHAPE", 3: "AQLM_ERR_SCHEME",
-                4: "AQLM_ERR_ALIGN", 5: "AQLM_ERR_BATCH", 6: "AQLM_ERR_HIP"}
+                4: "AQLM_ERR_ALIGN", 5: "AQLM_ERR_BATCH", 6: "AQLM_ERR_HIP",
+                7: "AQLM_ERR_WORKSPACE"}
 EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemv_batched", "aqlm_gemm",
-                    "aqlm_status_string", "aqlm_abi_version")
-ABI_VERSION = 2
+                    "aqlm_gemm_workspace_size", "aqlm_gemm_ws", "aqlm_status_string",
+                    "aqlm_abi_version")
+ABI_VERSION = 3
 AQLM_CODES_PACKED = 1
 SCHEMES = {(2, 8, 8): "2x8", (1, 16, 8): "1x16", (1, 16, 16): "1x16g16"}
 
@@ -72,6 +74,11 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [lp, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.aqlm_gemm_workspace_size.argtypes = [lp, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+    lib.aqlm_gemm_workspace_size.restype = ctypes.c_int
+    lib.aqlm_gemm_ws.argtypes = [lp, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.aqlm_gemm_ws.restype = ctypes.c_int
     lib.aqlm_gemv_batched.argtypes = [lp, ctypes.POINTER(ctypes.c_void_p),
                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                                       ctypes.c_int64, ctypes.c_void_p]
@@ -199,9 +206,38 @@ class AqlmLayer:
         """y = x . W^T for 1..8 activation rows (codebook-lookup path)."""
         return self._product("aqlm_gemv", x, out)
 
-    def gemm(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """y = x . W^T for any number of activation rows (matrix-core path)."""
-        return self._product("aqlm_gemm", x, out)
+    def workspace_bytes(self, batch: int) -> int:
+        """Device workspace aqlm_gemm_ws needs for this batch (0: none)."""
+        n = ctypes.c_int64(0)
+        _check(load_library().aqlm_gemm_workspace_size(ctypes.byref(self._struct), int(batch),
+                                                       ctypes.byref(n)))
+        return n.value
+
+    def gemm(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+             workspace: bool = True) -> torch.Tensor:
+        """y = x . W^T for any number of activation rows (matrix-core path).
+
+        With workspace=True (the default) the call goes through aqlm_gemm_ws
+        with a workspace taken from torch's allocator on the current stream;
+        workspace=False calls aqlm_gemm, which needs none.
+        """
+        if not workspace:
+            return self._product("aqlm_gemm", x, out)
+        lib = load_library()
+        x = self._check_x(x)
+        batch = x.shape[0]
+        if out is None:
+            out = torch.empty((batch, self.out_features), dtype=torch.float16, device=self.device)
+        elif (out.shape != (batch, self.out_features) or out.dtype != torch.float16
+              or not out.is_contiguous() or out.device != self.device):
+            raise ValueError("out must be a contiguous float16 [batch, out] tensor on the device")
+        need = self.workspace_bytes(batch)
+        ws = torch.empty(need, dtype=torch.uint8, device=self.device) if need else None
+        with torch.cuda.device(self.device):
+            _check(lib.aqlm_gemm_ws(ctypes.byref(self._struct), x.data_ptr(), batch,
+                                    out.data_ptr(), ws.data_ptr() if ws is not None else None,
+                                    need, _stream_handle(self.device)))
+        return out
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         """Pick the lookup path for <= 8 rows and the matrix-core path above."""

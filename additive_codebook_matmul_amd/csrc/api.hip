@@ -71,6 +71,7 @@ const char *aqlm_status_string(int status) {
     case AQLM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case AQLM_ERR_BATCH: return "batch outside the entry point's range";
     case AQLM_ERR_HIP: return "the HIP runtime reported an error";
+    case AQLM_ERR_WORKSPACE: return "the workspace is smaller than aqlm_gemm_workspace_size";
     default: return "unknown status";
   }
 }
@@ -113,18 +114,52 @@ int aqlm_gemv_batched(const aqlm_layer *layers, const uint16_t *const *x, uint16
                                             static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// batch range of the GEMM entry points (grid.y holds the activation-row tiles)
+bool gemm_batch_ok(int64_t batch) {
+  return batch >= 0 && batch <= (int64_t)INT_MAX / 2 && (batch + 63) / 64 <= 65535;
+}
+}  // namespace
+
 int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
               void *stream) {
   aqlm::LayerDesc d;
   const int st = check_layer(layer, &d);
   if (st != AQLM_OK) return st;
-  if (batch < 0 || batch > (int64_t)INT_MAX / 2) return AQLM_ERR_BATCH;
+  if (!gemm_batch_ok(batch)) return AQLM_ERR_BATCH;
   if (batch == 0) return AQLM_OK;
   if (!x || !y) return AQLM_ERR_NULL;
   if (!aligned16(x) || !aligned16(y)) return AQLM_ERR_ALIGN;
-  // grid.y holds the activation-row tiles
-  if ((batch + 63) / 64 > 65535) return AQLM_ERR_BATCH;
   return from_hip(aqlm::launch_gemm(d, x, batch, y, static_cast<hipStream_t>(stream)));
+}
+
+int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, int64_t *bytes) {
+  if (!bytes) return AQLM_ERR_NULL;
+  *bytes = 0;
+  aqlm::LayerDesc d;
+  const int st = check_layer(layer, &d);
+  if (st != AQLM_OK) return st;
+  if (!gemm_batch_ok(batch)) return AQLM_ERR_BATCH;
+  if (batch > 0) *bytes = aqlm::gemm_ws_bytes(d, batch);
+  return AQLM_OK;
+}
+
+int aqlm_gemm_ws(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
+                 void *workspace, int64_t workspace_bytes, void *stream) {
+  aqlm::LayerDesc d;
+  const int st = check_layer(layer, &d);
+  if (st != AQLM_OK) return st;
+  if (!gemm_batch_ok(batch)) return AQLM_ERR_BATCH;
+  if (batch == 0) return AQLM_OK;
+  if (!x || !y) return AQLM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return AQLM_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t need = aqlm::gemm_ws_bytes(d, batch);
+  if (need == 0) return from_hip(aqlm::launch_gemm(d, x, batch, y, s));
+  if (!workspace) return AQLM_ERR_NULL;
+  if (!aligned16(workspace)) return AQLM_ERR_ALIGN;
+  if (workspace_bytes < need) return AQLM_ERR_WORKSPACE;
+  return from_hip(aqlm::launch_gemm_ws(d, x, batch, y, workspace, s));
 }
 
 }  // extern "C"

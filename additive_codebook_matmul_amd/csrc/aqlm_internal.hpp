@@ -37,6 +37,12 @@ hipError_t launch_gemv(const LayerDesc &L, const uint16_t *x, int batch, uint16_
                        hipStream_t stream);
 hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                        hipStream_t stream);
+// Batched product with a caller-owned workspace (gemm_mid.hip): bytes the
+// workspace needs for this layer and batch (0: none, the call then runs
+// launch_gemm), and the launch itself.
+int64_t gemm_ws_bytes(const LayerDesc &L, int64_t batch);
+hipError_t launch_gemm_ws(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
+                          void *ws, hipStream_t stream);
 // Kernels for Scheme::kGeneral (general.hip).
 hipError_t launch_dequant_general(const LayerDesc &L, uint16_t *W, hipStream_t stream);
 hipError_t launch_gemv_general(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,

@@ -1,0 +1,442 @@
+// Batched product y = x . W^T for 17..128 activation rows with a caller-owned
+// device workspace (aqlm_gemm_ws). The weights are decoded on chip straight
+// into the A operand of v_mfma_f32_16x16x32_f16 (float32 accumulation) and
+// are never written to memory.
+//
+// Why a workspace. In the MFMA operand layout a lane holds 16 bytes of one
+// activation row, and the 16 lanes that hold one k-slice hold 16 different
+// rows. Loaded straight from x [batch][in], every lane of a wavefront touches
+// its own cache line and the vector L1 serves about one lane per clock. The
+// first launch (gemm_xblock_kernel) therefore re-lays x into k-blocks of 8
+// inputs,
+//   xb[kb][t][0..7] = x[t][8 kb .. 8 kb + 7]    (t < BP = 16 NT, zero past batch),
+// after which the B operand of one MFMA step for 16 activation rows is one
+// contiguous 256-byte run. The workspace also holds the float32 partial tiles
+// of the split-K form below.
+//
+// Tiles. A workgroup of four wavefronts owns RT tiles of 16 output rows and
+// all BP activation rows (NT tiles of 16): each decoded A operand feeds NT
+// MFMAs and each B operand RT MFMAs. K is walked in super-chunks of 32 groups
+// (256 inputs for g = 8, 512 for g = 16). Within a super-chunk, lane quarter q
+// owns groups 8q .. 8q+7 -- one 16-byte load of codes per row tile -- and in
+// MFMA step s it feeds k-block g q + s of the super-chunk, in A and in B
+// alike, so the sum is unchanged. The four wavefronts take every fourth
+// super-chunk of the workgroup's K range and add their float32 partial tiles
+// in LDS in wavefront order at the end.
+//
+// Split-K. When the row blocks alone are too few to fill the chip, the K
+// range is cut into `splits` parts (workgroup = row block * splits + part).
+// Every workgroup then writes its float32 partial tile to the workspace and a
+// third launch (gemm_mid_reduce_kernel) adds the parts of each output in part
+// order, scales and writes y: deterministic, and free of cross-workgroup
+// synchronisation (a device-scope release inside the kernel would write back
+// the whole L2 of the XCD once per workgroup). With splits dividing 8, part k
+// of every row block runs on XCD k mod 8, so each XCD's L2 holds only its
+// share of xb.
+//
+// Pipelining: codes one super-chunk ahead; B operands (and the 1x16 codewords,
+// gathered from the L2-resident codebook) D steps ahead in register rings; the
+// 2x8 A operands one step ahead from an 8 KiB LDS copy of the codebooks. Every
+// load of codes and activations is an unconditional buffer load whose
+// out-of-range offsets read zero (codeword 0 times zero activations adds 0).
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
+#include "aqlm_device.hpp"
+
+namespace aqlm {
+namespace {
+
+constexpr int kMidWaves = 4;
+constexpr int kMidThreads = 64 * kMidWaves;
+constexpr int kGroupsPerSc = 32;  // groups per super-chunk
+constexpr uint32_t kMidOOB = 0x80000000u;
+constexpr int64_t kMidMinBatch = 17;  // up to 16 rows the skinny kernel of aqlm_gemm is as fast
+constexpr int64_t kMidMaxBatch = 128;
+constexpr int kMidCus = 256;
+constexpr int kMidOccupancy = 1;  // wavefronts per SIMD the kernel is built for
+constexpr int kMidMaxTiles = 32;  // largest RT * NT (accumulator tiles per wavefront)
+
+template <Scheme S>
+struct MidCfg {
+  static constexpr int G = group_size(S);
+  static constexpr int STEPS = G;          // MFMA steps per super-chunk
+  static constexpr int SC_BLOCKS = 4 * G;  // k-blocks of 8 inputs per super-chunk
+};
+
+// B-ring depth: enough steps ahead to cover ~1000 clocks of MFMA work.
+constexpr int ring_depth(int rt, int nt) { return rt * nt >= 16 ? 2 : rt * nt >= 8 ? 4 : 8; }
+
+constexpr size_t mid_lds_bytes(bool lut, int rt, int nt) {
+  return (lut ? 8192 : 0) + (size_t)kMidWaves * rt * nt * 1024;
+}
+
+// Code of step s (a compile-time constant) from a lane's 16 code bytes: g = 8
+// steps walk the 8 groups, g = 16 steps take each group twice.
+template <int G>
+__device__ __forceinline__ uint32_t code_of(const uint4 &cw, int s) {
+  const int gi = G == 8 ? s : s >> 1;
+  const int d = gi >> 1;
+  const uint32_t word = d == 0 ? cw.x : d == 1 ? cw.y : d == 2 ? cw.z : cw.w;
+  return (gi & 1) ? word >> 16 : word & 0xFFFFu;
+}
+
+__global__ __launch_bounds__(256) void gemm_xblock_kernel(const uint4 *__restrict__ x,
+                                                          uint4 *__restrict__ xb, int nkb,
+                                                          int batch, int bp) {
+  // 16 activation rows x 16 k-blocks through LDS: rows are read and k-blocks
+  // written as 256-byte runs (the +1 column keeps the transposed read free of
+  // bank conflicts)
+  __shared__ uint4 tile[16][17];
+  const int i = threadIdx.x;
+  const int kb0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  {
+    const int t = t0 + (i >> 4), kb = kb0 + (i & 15);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (t < batch && kb < nkb) v = x[(size_t)t * nkb + kb];
+    tile[i >> 4][i & 15] = v;
+  }
+  __syncthreads();
+  {
+    const int kb = kb0 + (i >> 4), t = t0 + (i & 15);
+    if (kb < nkb) xb[(size_t)kb * bp + t] = tile[i & 15][i >> 4];
+  }
+}
+
+// Output element e of row block rb: accumulator (t, j) = e / 64 of the
+// 16 x 16 tiles, lane e % 64 (rows 4 (lane / 16) .. + 3, activation row lane % 16).
+template <int NT>
+__device__ __forceinline__ void store_out(uint16_t *__restrict__ y,
+                                          const uint16_t *__restrict__ scales, int out, int batch,
+                                          int row0, int e, float4_t v) {
+  const int tj = e >> 6, l = e & 63;
+  const int t = tj / NT, j = tj - t * NT;
+  const int tok = j * 16 + (l & 15);
+  if (tok >= batch) return;
+  const int row = row0 + t * 16 + 4 * (l >> 4);
+  uint16_t *dst = y + (int64_t)tok * out + row;
+  if ((out & 3) == 0 && row + 3 < out) {
+    const uint32_t h0 = f2h(v[0] * h2f(scales[row])) | (f2h(v[1] * h2f(scales[row + 1])) << 16);
+    const uint32_t h1 = f2h(v[2] * h2f(scales[row + 2])) | (f2h(v[3] * h2f(scales[row + 3])) << 16);
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(h0, h1);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (row + k < out) dst[k] = (uint16_t)f2h(v[k] * h2f(scales[row + k]));
+  }
+}
+
+// Split-K epilogue: the parts of each element added in part order.
+template <int RT, int NT>
+__global__ __launch_bounds__(256) void gemm_mid_reduce_kernel(const float4_t *__restrict__ part,
+                                                              const uint16_t *__restrict__ scales,
+                                                              uint16_t *__restrict__ y, int out,
+                                                              int batch, int splits) {
+  constexpr int E = RT * NT * 64;
+  const int rb = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const float4_t *p = part + (size_t)rb * splits * E + e;
+  float4_t v = p[0];
+  for (int k = 1; k < splits; ++k) v += p[(size_t)k * E];
+  store_out<NT>(y, scales, out, batch, rb * 16 * RT, e, v);
+}
+
+template <Scheme S, int RT, int NT>
+__global__ __launch_bounds__(kMidThreads)
+__attribute__((amdgpu_waves_per_eu(kMidOccupancy, kMidOccupancy)))
+void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
+                     const uint16_t *__restrict__ scales, const uint4 *__restrict__ xb,
+                     uint16_t *__restrict__ y, float4_t *__restrict__ part, int out, int groups,
+                     int batch, int splits, uint32_t codes_bytes, uint32_t xb_bytes) {
+  using C = MidCfg<S>;
+  constexpr int G = C::G, STEPS = C::STEPS;
+  constexpr bool LUT = S == Scheme::k2x8;
+  constexpr int BP = 16 * NT;
+  constexpr int E = RT * NT * 64;  // float4 accumulators of a workgroup tile
+  constexpr int D = ring_depth(RT, NT);
+  static_assert(STEPS % D == 0, "the ring depth divides the steps of a super-chunk");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint4 *lds_books = reinterpret_cast<uint4 *>(lds);
+  float4_t *red = reinterpret_cast<float4_t *>(lds + (LUT ? 8192 : 0));
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int sp = (int)(blockIdx.x % (unsigned)splits), rb = (int)(blockIdx.x / (unsigned)splits);
+  const int row0 = rb * 16 * RT;
+  const int nsc = (groups + kGroupsPerSc - 1) / kGroupsPerSc;
+  const int sc_end = (int)((int64_t)(sp + 1) * nsc / splits);
+  const uint32_t row_bytes = (uint32_t)groups * 2u;
+  const Rsrc crs = make_rsrc(codes, codes_bytes);
+  const Rsrc xrs = make_rsrc(xb, xb_bytes);
+  const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
+
+  const uint32_t code_lane = (uint32_t)(row0 + r) * row_bytes + (uint32_t)q * 16u;
+  const uint32_t x_lane = ((uint32_t)(q * G * BP) + (uint32_t)r) * 16u;
+  constexpr uint32_t kBlockBytes = BP * 16u;  // one k-block of xb
+  constexpr uint32_t kScXBytes = C::SC_BLOCKS * kBlockBytes;
+
+  // this lane's 16 code bytes of super-chunk sc for every row tile
+  auto load_codes = [&](int sc, uint4 (&cw)[RT]) __attribute__((always_inline)) {
+    const bool ok = sc < sc_end && sc * kGroupsPerSc + 8 * q < groups;
+    const uint32_t base = ok ? code_lane + (uint32_t)sc * (kGroupsPerSc * 2u) : kMidOOB;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) cw[t] = buf_load16(crs, base + (uint32_t)t * 16u * row_bytes);
+  };
+  // B operands of step s of super-chunk sc (k-block g q + s, rows 16 j + r)
+  auto load_x = [&](int sc, int s, uint4 (&bx)[NT]) __attribute__((always_inline)) {
+    const uint32_t base =
+        sc < sc_end ? x_lane + (uint32_t)sc * kScXBytes + (uint32_t)s * kBlockBytes : kMidOOB;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) bx[j] = buf_load16(xrs, base + (uint32_t)j * 256u);
+  };
+  // 1x16: this lane's codeword (half, for g = 16) of step s
+  auto gather = [&](const uint4 (&cw)[RT], int s, uint4 (&ga)[RT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const uint32_t code = code_of<G>(cw[t], s);
+      ga[t] = gbooks[G == 8 ? code : 2u * code + (uint32_t)(s & 1)];
+    }
+  };
+  // 2x8: the fp16 sum of the two codewords of step s
+  auto decode = [&](const uint4 (&cw)[RT], int s, uint4 (&a)[RT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const uint32_t code = code_of<G>(cw[t], s);
+      a[t] = hadd8(lds_books[code & 0xFFu], lds_books[256u + (code >> 8)]);
+    }
+  };
+
+  float4_t acc[RT][NT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[t][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  int sc = (int)((int64_t)sp * nsc / splits) + w;
+  uint4 cw[2][RT];  // codes of this and of the wave's next super-chunk (static ring)
+  uint4 bx[D][NT];
+  uint4 ga[LUT ? 1 : D][RT];
+  uint4 a[2][RT];
+  load_codes(sc, cw[0]);
+  load_codes(sc + kMidWaves, cw[1]);
+#pragma unroll
+  for (int i = 0; i < D; ++i) load_x(sc, i, bx[i]);
+  if constexpr (LUT) {
+    for (int i = tid; i < 512; i += kMidThreads) lds_books[i] = gbooks[i];
+    __syncthreads();
+    decode(cw[0], 0, a[0]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) gather(cw[0], i, ga[i]);
+  }
+
+  // one super-chunk whose codes are in cw[K] (the next one's in cw[K ^ 1]);
+  // the refilled code slot is cw[K], for the super-chunk after the next
+  auto super_chunk = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int K = decltype(kc)::value;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      const int slot = s % D;
+      if constexpr (LUT) {
+        // A operands of the next step first, so their LDS reads overlap this step's MFMAs
+        if (s + 1 < STEPS)
+          decode(cw[K], s + 1, a[(s + 1) & 1]);
+        else
+          decode(cw[K ^ 1], 0, a[(s + 1) & 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint4 at = LUT ? a[s & 1][t] : ga[LUT ? 0 : slot][t];
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, at),
+                                                            __builtin_bit_cast(half8_t, bx[slot][j]),
+                                                            acc[t][j], 0, 0, 0);
+      }
+      // refill the slot with step s + D (in the wave's next super-chunk past the end of this one)
+      if (s + D < STEPS) {
+        load_x(sc, s + D, bx[slot]);
+        if constexpr (!LUT) gather(cw[K], s + D, ga[slot]);
+      } else {
+        load_x(sc + kMidWaves, s + D - STEPS, bx[slot]);
+        if constexpr (!LUT) gather(cw[K ^ 1], s + D - STEPS, ga[slot]);
+      }
+    }
+    load_codes(sc + 2 * kMidWaves, cw[K]);
+    sc += kMidWaves;
+  };
+  while (sc < sc_end) {
+    super_chunk(std::integral_constant<int, 0>{});
+    if (sc >= sc_end) break;
+    super_chunk(std::integral_constant<int, 1>{});
+  }
+
+  // the four wavefronts' partial tiles, added in wavefront order
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) red[((w * RT + t) * NT + j) * 64 + lane] = acc[t][j];
+  __syncthreads();
+
+  auto wave_sum = [&](int e) __attribute__((always_inline)) {
+    float4_t v = red[e] + red[E + e];
+    v += red[2 * E + e];
+    v += red[3 * E + e];
+    return v;
+  };
+  if (splits == 1) {
+    for (int e = tid; e < E; e += kMidThreads)
+      store_out<NT>(y, scales, out, batch, row0, e, wave_sum(e));
+  } else {
+    float4_t *mine = part + ((size_t)rb * splits + sp) * E;
+    for (int e = tid; e < E; e += kMidThreads) mine[e] = wave_sum(e);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Plan: activation tiles, row tiles per workgroup and K parts, chosen by a
+// clock model of one workgroup step round (four wavefronts, one MFMA step
+// each) -- MFMA issue, L1 accesses (one per 64-byte run a lane quad touches),
+// LDS codebook reads (2x8) or L2 codeword gathers (1x16) -- times the steps
+// per wavefront, times the rounds of workgroups over the CUs.
+struct MidPlan {
+  int nt = 0, rt = 0, splits = 0, nrb = 0;
+  size_t xb_bytes = 0, part_off = 0, total = 0;
+};
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int mid_nt(int64_t batch) {
+  const int n = (int)((batch + 15) / 16);
+  return n <= 4 ? n : n <= 6 ? 6 : 8;
+}
+
+bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
+  if (L.scheme == Scheme::kGeneral || L.packed || batch < kMidMinBatch || batch > kMidMaxBatch)
+    return false;
+  if (L.groups % 8 != 0) return false;  // a lane's 16 code bytes never straddle a row end
+  const int G = group_size(L.scheme);
+  const int steps = G;
+  const int nt = mid_nt(batch);
+  const int64_t bp = 16 * nt;
+  const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
+  const int64_t nsc = (L.groups + kGroupsPerSc - 1) / kGroupsPerSc;
+  const int64_t xb_bytes = L.in * bp * 2;
+  // 32-bit buffer offsets, with room for the out-of-range marker
+  if ((L.out + 64) * row_bytes >= (int64_t(1) << 31) || xb_bytes + 4 * 65536 >= (int64_t(1) << 31))
+    return false;
+  double best = 0;
+  for (int rt : {4, 2}) {
+    if (rt * nt > kMidMaxTiles) continue;
+    const int64_t nrb = (L.out + 16 * rt - 1) / (16 * rt);
+    const double mfma = 16.0 * rt * nt;
+    const double l1 = kMidWaves * (16.0 * nt + 64.0 * rt / steps);
+    const double dec = L.scheme == Scheme::k2x8 ? kMidWaves * 40.0 * rt : kMidWaves * 150.0 * rt;
+    const double round = std::max(std::max(mfma, l1), dec);
+    for (int splits : {1, 2, 4, 8}) {
+      if (splits > 1 && splits * 2 > nsc) break;
+      const int64_t sc_per_wave = ((nsc + splits - 1) / splits + kMidWaves - 1) / kMidWaves;
+      const double wg = sc_per_wave * steps * round +
+                        (splits > 1 ? 2000.0 + 16.0 * rt * nt : 0.0);
+      const int64_t rounds = (nrb * splits + kMidCus * kMidOccupancy - 1) / (kMidCus * kMidOccupancy);
+      const double t = rounds * wg;
+      if (p->nt == 0 || t < best) {
+        best = t;
+        p->nt = nt;
+        p->rt = rt;
+        p->splits = splits;
+        p->nrb = (int)nrb;
+      }
+    }
+  }
+  if (p->nt == 0) return false;
+  p->xb_bytes = (size_t)xb_bytes;
+  p->part_off = align256((size_t)xb_bytes);
+  p->total = p->part_off + (p->splits > 1 ? (size_t)p->nrb * p->splits * p->rt * p->nt * 1024 : 0);
+  return p->total < (size_t(1) << 40);
+}
+
+template <Scheme S, int RT, int NT>
+hipError_t launch_mid_t(const LayerDesc &L, const MidPlan &P, const uint16_t *x, int64_t batch,
+                        uint16_t *y, uint8_t *ws, hipStream_t stream) {
+  constexpr bool LUT = S == Scheme::k2x8;
+  constexpr size_t lds = mid_lds_bytes(LUT, RT, NT);
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto k = gemm_mid_kernel<S, RT, NT>;
+  if (lds > 64 * 1024) {
+    // more than the default dynamic LDS limit: raise it once per device
+    static std::atomic<uint64_t> raised{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = uint64_t(1) << (dev & 63);
+    if (dev >= 64 || !(raised.load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      raised.fetch_or(bit, std::memory_order_acq_rel);
+    }
+  }
+  uint4 *xb = reinterpret_cast<uint4 *>(ws);
+  float4_t *part = reinterpret_cast<float4_t *>(ws + P.part_off);
+  const int nkb = (int)(L.in / 8);
+  hipLaunchKernelGGL(gemm_xblock_kernel, dim3((unsigned)((nkb + 15) / 16), (unsigned)NT),
+                     dim3(256), 0, stream, reinterpret_cast<const uint4 *>(x), xb, nkb, (int)batch,
+                     16 * NT);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((unsigned)(P.nrb * P.splits)), dim3(kMidThreads), lds, stream,
+                     static_cast<const uint8_t *>(L.codes), L.books, L.scales, xb, y, part,
+                     (int)L.out, (int)L.groups, (int)batch, P.splits,
+                     (uint32_t)(L.out * L.groups * kCodeBytesPerGroup), (uint32_t)P.xb_bytes);
+  e = hipGetLastError();
+  if (e != hipSuccess || P.splits == 1) return e;
+  constexpr int E = RT * NT * 64;
+  hipLaunchKernelGGL((gemm_mid_reduce_kernel<RT, NT>), dim3((unsigned)((E + 255) / 256),
+                     (unsigned)P.nrb), dim3(256), 0, stream, part, L.scales, y, (int)L.out,
+                     (int)batch, P.splits);
+  return hipGetLastError();
+}
+
+template <Scheme S, int NT>
+hipError_t launch_mid_nt(const LayerDesc &L, const MidPlan &P, const uint16_t *x, int64_t batch,
+                         uint16_t *y, uint8_t *ws, hipStream_t stream) {
+  return P.rt == 4 ? launch_mid_t<S, 4, NT>(L, P, x, batch, y, ws, stream)
+                   : launch_mid_t<S, 2, NT>(L, P, x, batch, y, ws, stream);
+}
+
+template <Scheme S>
+hipError_t launch_mid_s(const LayerDesc &L, const MidPlan &P, const uint16_t *x, int64_t batch,
+                        uint16_t *y, uint8_t *ws, hipStream_t stream) {
+  switch (P.nt) {
+    case 2: return launch_mid_nt<S, 2>(L, P, x, batch, y, ws, stream);
+    case 3: return launch_mid_nt<S, 3>(L, P, x, batch, y, ws, stream);
+    case 4: return launch_mid_nt<S, 4>(L, P, x, batch, y, ws, stream);
+    case 6: return launch_mid_nt<S, 6>(L, P, x, batch, y, ws, stream);
+    default: return launch_mid_nt<S, 8>(L, P, x, batch, y, ws, stream);
+  }
+}
+
+}  // namespace
+
+int64_t gemm_ws_bytes(const LayerDesc &L, int64_t batch) {
+  MidPlan p;
+  return mid_plan(L, batch, &p) ? (int64_t)p.total : 0;
+}
+
+hipError_t launch_gemm_ws(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
+                          void *ws, hipStream_t stream) {
+  MidPlan p;
+  if (!mid_plan(L, batch, &p)) return launch_gemm(L, x, batch, y, stream);
+  uint8_t *w = static_cast<uint8_t *>(ws);
+  switch (L.scheme) {
+    case Scheme::k2x8: return launch_mid_s<Scheme::k2x8>(L, p, x, batch, y, w, stream);
+    case Scheme::k1x16: return launch_mid_s<Scheme::k1x16>(L, p, x, batch, y, w, stream);
+    default: return launch_mid_s<Scheme::k1x16g16>(L, p, x, batch, y, w, stream);
+  }
+}
+
+}  // namespace aqlm

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define AQLM_ABI_VERSION 2
+#define AQLM_ABI_VERSION 3
 
 /* aqlm_layer.flags: codes are bit-packed (see the format above). */
 #define AQLM_CODES_PACKED 1
@@ -86,7 +86,8 @@ typedef enum aqlm_status {
   AQLM_ERR_SCHEME = 3, /* (M, B, g) is not a supported scheme */
   AQLM_ERR_ALIGN = 4,  /* a pointer is not 16-byte aligned */
   AQLM_ERR_BATCH = 5,  /* batch outside the entry point's range */
-  AQLM_ERR_HIP = 6     /* the HIP runtime reported an error at launch */
+  AQLM_ERR_HIP = 6,    /* the HIP runtime reported an error at launch */
+  AQLM_ERR_WORKSPACE = 7 /* the workspace is smaller than aqlm_gemm_workspace_size */
 } aqlm_status;
 
 /* One quantized layer: sizes plus device pointers to the packed arrays. */
@@ -132,6 +133,40 @@ AQLM_API int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch
  */
 AQLM_API int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
               uint16_t *y, void *stream);
+
+/*
+ * aqlm_gemm_workspace_size: bytes of device workspace that aqlm_gemm_ws needs
+ * for this layer and batch, written to *bytes (0 when that call needs none
+ * and runs exactly as aqlm_gemm). The size depends only on the layer's shape
+ * and scheme and on batch. Validation and status codes as for aqlm_gemm;
+ * *bytes is 0 on error.
+ */
+AQLM_API int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, int64_t *bytes);
+
+/*
+ * aqlm_gemm_ws: the product of aqlm_gemm with a caller-owned device
+ * workspace, which lets batches of 17..128 activation rows of the three
+ * dedicated schemes (2x8, 1x16 and 1x16 with g = 16; element codes, in / g a
+ * multiple of 8) run the workspace form of the matrix-core path: the
+ * activations are first re-laid into blocks of 8 inputs so that every MFMA
+ * operand load is contiguous, and K may be split across workgroups whose
+ * float32 partial sums meet in the workspace. Every other case runs as
+ * aqlm_gemm and ignores the workspace.
+ *   workspace        device pointer, 16-byte aligned, at least
+ *                    aqlm_gemm_workspace_size bytes (NULL allowed when that
+ *                    size is 0); overwritten by the call; must not overlap
+ *                    x or y
+ *   workspace_bytes  its size in bytes
+ * The result is deterministic for a given layer shape and batch (the split
+ * parts are added in a fixed order whatever order they finish in) but is
+ * not bit-identical to aqlm_gemm, which sums in another order; both meet the
+ * same tolerance. Calls on different streams need different workspaces.
+ * Returns AQLM_ERR_WORKSPACE if workspace_bytes is too small, AQLM_ERR_NULL
+ * if the workspace is needed and NULL, AQLM_ERR_ALIGN if it is misaligned;
+ * otherwise as aqlm_gemm.
+ */
+AQLM_API int aqlm_gemm_ws(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
+                          void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * aqlm_gemv_batched: aqlm_gemv for num_layers independent layers in one call:

@@ -51,7 +51,7 @@ def test_struct_layout_matches_header():
 
 
 def test_status_strings():
-    for st in range(7):
+    for st in range(8):
         assert _lib.status_string(st)
     assert _lib.status_string(99) == "unknown status"
     assert _lib.status_string(0) == "ok"
@@ -65,6 +65,8 @@ ENTRY = {
     "aqlm_dequant": lambda s, x, b, y: _lib.raw_call("aqlm_dequant", s, y, None),
     "aqlm_gemv": lambda s, x, b, y: _lib.raw_call("aqlm_gemv", s, x, b, y, None),
     "aqlm_gemm": lambda s, x, b, y: _lib.raw_call("aqlm_gemm", s, x, b, y, None),
+    "aqlm_gemm_ws": lambda s, x, b, y: _lib.raw_call("aqlm_gemm_ws", s, x, b, y, FAKE, 1 << 40,
+                                                     None),
 }
 
 
@@ -74,6 +76,8 @@ def test_null_layer_pointer(fn):
     f = getattr(lib, fn)
     if fn == "aqlm_dequant":
         assert f(None, FAKE, None) == 1
+    elif fn == "aqlm_gemm_ws":
+        assert f(None, FAKE, 1, FAKE, FAKE, 1 << 40, None) == 1
     else:
         assert f(None, FAKE, 1, FAKE, None) == 1
 
@@ -100,7 +104,7 @@ def test_output_pointer_validation(fn):
     assert ENTRY[fn](s, FAKE, 1, MISALIGNED) == 4
 
 
-@pytest.mark.parametrize("fn", ["aqlm_gemv", "aqlm_gemm"])
+@pytest.mark.parametrize("fn", ["aqlm_gemv", "aqlm_gemm", "aqlm_gemm_ws"])
 def test_input_pointer_and_batch_validation(fn):
     s = _layer()
     assert ENTRY[fn](s, 0, 1, FAKE) == 1
@@ -114,6 +118,47 @@ def test_batch_limits():
     s = _layer()
     assert ENTRY["aqlm_gemv"](s, FAKE, 9, FAKE) == 5
     assert ENTRY["aqlm_gemm"](s, FAKE, 1 << 40, FAKE) == 5
+    assert ENTRY["aqlm_gemm_ws"](s, FAKE, 1 << 40, FAKE) == 5
+
+
+def _ws_size(s, batch):
+    n = ctypes.c_int64(-1)
+    st = _lib.load_library().aqlm_gemm_workspace_size(ctypes.byref(s), batch, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size():
+    """Host-side sizing: the workspace form covers 17..128 rows of the three
+    dedicated schemes with element codes and in/g a multiple of 8; it holds at
+    least the re-laid activations (in x 16*ceil(batch/16) float16 values)."""
+    mlp = dict(out=4096, n_in=11008)
+    for M, B, g in ((2, 8, 8), (1, 16, 8), (1, 16, 16)):
+        for batch in (17, 33, 64, 100, 128):
+            st, n = _ws_size(_layer(M, B, g, **mlp), batch)
+            bp = 16 * min(8, {5: 6, 7: 8}.get((batch + 15) // 16, (batch + 15) // 16))
+            assert st == 0 and n >= 11008 * bp * 2, (M, B, g, batch, n)
+            assert n % 16 == 0
+    assert _ws_size(_layer(**mlp), 0) == (0, 0)
+    assert _ws_size(_layer(**mlp), 16) == (0, 0)                     # skinny tiles need none
+    assert _ws_size(_layer(**mlp), 129) == (0, 0)                    # wide tiles need none
+    assert _ws_size(_layer(3, 8, 8, **mlp), 64) == (0, 0)            # general scheme
+    assert _ws_size(_layer(flags=1, **mlp), 64) == (0, 0)            # bit-packed codes
+    assert _ws_size(_layer(out=64, n_in=36 * 8), 64) == (0, 0)       # in/g not a multiple of 8
+    assert _ws_size(_layer(codes=0, **mlp), 64) == (1, 0)
+    assert _ws_size(_layer(**mlp), -1) == (5, 0)
+    assert _lib.load_library().aqlm_gemm_workspace_size(ctypes.byref(_layer()), 1, None) == 1
+
+
+def test_workspace_validation():
+    """Errors of aqlm_gemm_ws that stop the call before any launch."""
+    s = _layer(out=4096, n_in=11008)
+    st, need = _ws_size(s, 64)
+    assert st == 0 and need > 0
+    f = _lib.load_library().aqlm_gemm_ws
+    assert f(ctypes.byref(s), FAKE, 64, FAKE, None, need, None) == 1
+    assert f(ctypes.byref(s), FAKE, 64, FAKE, MISALIGNED, need, None) == 4
+    assert f(ctypes.byref(s), FAKE, 64, FAKE, FAKE, need - 1, None) == 7
+    assert f(ctypes.byref(s), FAKE, 0, FAKE, None, 0, None) == 0     # batch 0: no-op
 
 
 def test_binding_rejects_cpu_tensors_without_calling_the_library():

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from additive_codebook_matmul_amd import AqlmLayer, workloads as WL
+from additive_codebook_matmul_amd import AqlmLayer, _lib, workloads as WL
 from gpu_util import (assert_bit_exact, assert_product, bits, dev_layer, dev_x, device,
                       to_dev_codes)
 
@@ -26,9 +26,10 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 SCHEMES = {"2x8": WL.S2x8, "1x16": WL.S1x16, "1x16g16": WL.S1x16g16}
 
 # (out, groups): single row/group, ragged rows and groups, multiples of the
-# 16-byte code chunk (8 groups) with and without row tails, several tiles.
+# 16-byte code chunk (8 groups) with and without row tails, several tiles, and
+# whole 256-input chunks (the mid-batch GEMM) with ragged rows.
 SMALL_SHAPES = [(1, 1), (7, 5), (64, 8), (255, 13), (300, 64), (33, 172), (513, 24), (257, 9),
-                (70, 200)]
+                (70, 200), (77, 96), (1000, 32), (90, 48)]
 
 
 def _small(scheme, out, J, batch, seed):
@@ -71,10 +72,11 @@ def test_small_gemm(sname, out, J):
     s = SCHEMES[sname]
     codes, books, scales, x = _small(s, out, J, 130, seed=out * 23 + J)
     layer = dev_layer(codes, books, scales)
-    for batch in (1, 5, 16, 17, 32, 33, 64, 65, 130):
-        y = layer.gemm(dev_x(x[:batch]))
+    for batch in (1, 5, 16, 17, 32, 33, 64, 65, 100, 128, 130):
         y_ref, bound = oracle.forward(x[:batch], codes, books, scales)
-        assert_product(y, y_ref, bound, f"gemm {sname} {out}x{J} b{batch}")
+        for ws in (True, False):
+            y = layer.gemm(dev_x(x[:batch]), workspace=ws)
+            assert_product(y, y_ref, bound, f"gemm {sname} {out}x{J} b{batch} ws={ws}")
 
 
 # ---------------------------------------------------------------------------
@@ -186,19 +188,48 @@ def test_workload_gemv(wname, lname, batch):
         assert_product(y, y_ref, bound, f"{wname}/{lname} b{batch}")
 
 
+# the workload's batches plus batches of the mid-size GEMM (33..128 rows:
+# four row tiles per workgroup at 33/64 on the 11008-row layers, a half
+# chunk at the end of the 11008-input rows)
 GEMM_IDS = [(l.name, b) for l in WL.WORKLOADS["gemm_mlp"].layers
-            for b in WL.WORKLOADS["gemm_mlp"].batches]
+            for b in sorted(set(WL.WORKLOADS["gemm_mlp"].batches) | {33, 64, 100})]
 
 
 @pytest.mark.parametrize("lname,batch", GEMM_IDS, ids=lambda v: str(v))
 def test_workload_gemm(lname, batch):
     layer, d = _layer_data("gemm_mlp", lname)
     x = WL.make_x(layer, batch)
-    y = dev_layer(d.codes, d.codebooks, d.scales).gemm(dev_x(x)).cpu().numpy()
+    L = dev_layer(d.codes, d.codebooks, d.scales)
     toks = np.arange(batch) if batch <= 128 else np.unique(np.concatenate(
         [[0, batch - 1], np.random.default_rng(1).choice(batch, 62, replace=False)]))
     y_ref, bound = oracle.forward(x[toks], d.codes, d.codebooks, d.scales)
-    assert_product(y[toks], y_ref, bound, f"gemm {lname} b{batch}")
+    for ws in ((True, False) if batch <= 128 else (True,)):
+        y = L.gemm(dev_x(x), workspace=ws).cpu().numpy()
+        assert_product(y[toks], y_ref, bound, f"gemm {lname} b{batch} ws={ws}")
+
+
+@pytest.mark.parametrize("sname", list(SCHEMES))
+@pytest.mark.parametrize("out,n_in,batch", [(100, 16384, 40), (40, 32768, 128), (1000, 8192, 20)])
+def test_gemm_split_k(sname, out, n_in, batch):
+    """Few output rows over a long K: the workspace form splits K across
+    workgroups and the last one to finish a row block adds the parts. Two calls
+    in a row (the arrival counters are re-zeroed per call) give the same bits."""
+    s = SCHEMES[sname]
+    codes, books, scales, x = WL.small_case(out, n_in, s, batch, seed=out + batch)
+    layer = dev_layer(codes, books, scales)
+    y_ref, bound = oracle.forward(x, codes, books, scales)
+    ws = torch.empty(layer.workspace_bytes(batch), dtype=torch.uint8, device=device())
+    nt = -(-batch // 16)
+    assert ws.numel() > n_in * 16 * (nt if nt <= 4 else 8 if nt > 6 else 6) * 2 + 512  # K is split
+    ys = []
+    for _ in range(2):
+        y = torch.empty((batch, out), dtype=torch.float16, device=device())
+        assert _lib.raw_call("aqlm_gemm_ws", layer._struct, dev_x(x).data_ptr(), batch,
+                             y.data_ptr(), ws.data_ptr(), ws.numel(), None) == 0
+        torch.cuda.synchronize()
+        assert_product(y, y_ref, bound, f"split-K gemm {sname} {out}x{n_in} b{batch}")
+        ys.append(bits(y))
+    assert np.array_equal(ys[0], ys[1])
 
 
 # ---------------------------------------------------------------------------
@@ -231,10 +262,12 @@ def test_deterministic(sname):
     s = SCHEMES[sname]
     codes, books, scales, x = WL.small_case(2000, 2048, s, 64, seed=5)
     layer = dev_layer(codes, books, scales)
-    for fn, xb in ((layer.gemv, x[:8]), (layer.gemm, x)):
+    gemm_plain = lambda v: layer.gemm(v, workspace=False)  # noqa: E731
+    for name, fn, xb in (("gemv", layer.gemv, x[:8]), ("gemm_ws", layer.gemm, x),
+                         ("gemm", gemm_plain, x)):
         a = bits(fn(dev_x(xb)))
         b = bits(fn(dev_x(xb)))
-        assert np.array_equal(a, b), fn.__name__
+        assert np.array_equal(a, b), name
 
 
 @pytest.mark.parametrize("sname", list(SCHEMES))
@@ -253,6 +286,28 @@ def test_outputs_stay_in_bounds(sname):
     wbuf = torch.full((out * n_in + 64,), float(canary), dtype=torch.float16, device=device())
     layer.dequant(out=wbuf[: out * n_in].view(out, n_in))
     assert torch.all(wbuf[out * n_in:] == float(canary))
+
+
+@pytest.mark.parametrize("sname", list(SCHEMES))
+def test_workspace_form_stays_in_bounds(sname):
+    """The workspace form writes y and at most its workspace: canary words after
+    both stay untouched (ragged rows and activation rows, split and unsplit)."""
+    s = SCHEMES[sname]
+    canary = np.float16(-12345.0)
+    for out, n_in, batch in ((300, 64 * s.g, 37), (20, 512 * s.g, 70)):
+        codes, books, scales, x = WL.small_case(out, n_in, s, batch, seed=out)
+        layer = dev_layer(codes, books, scales)
+        need = layer.workspace_bytes(batch)
+        assert need > 0
+        ybuf = torch.full((batch * out + 64,), float(canary), dtype=torch.float16, device=device())
+        wbuf = torch.full(((need + 256) // 2,), float(canary), dtype=torch.float16, device=device())
+        assert _lib.raw_call("aqlm_gemm_ws", layer._struct, dev_x(x).data_ptr(), batch,
+                             ybuf.data_ptr(), wbuf.data_ptr(), need, None) == 0
+        torch.cuda.synchronize()
+        assert torch.all(ybuf[batch * out:] == float(canary))
+        assert torch.all(wbuf[(need + 1) // 2:] == float(canary))
+        y_ref, bound = oracle.forward(x, codes, books, scales)
+        assert_product(ybuf[: batch * out].view(batch, out), y_ref, bound, f"{sname} {out}x{n_in}")
 
 
 def test_zero_batch_is_noop():
