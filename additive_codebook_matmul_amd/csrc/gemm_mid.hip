@@ -36,9 +36,16 @@
 //
 // Pipelining: codes one super-chunk ahead; B operands (and the 1x16 codewords,
 // gathered from the L2-resident codebook) D steps ahead in register rings; the
-// 2x8 A operands one step ahead from an 8 KiB LDS copy of the codebooks. Every
-// load of codes and activations is an unconditional buffer load whose
-// out-of-range offsets read zero (codeword 0 times zero activations adds 0).
+// 2x8 A operands one step ahead from LDS. Every load of codes and activations
+// is an unconditional buffer load whose out-of-range offsets read zero
+// (codeword 0 times zero activations adds 0).
+//
+// 2x8 codebooks in LDS: a 64 KiB bank-spread table. The 256-byte stripe of
+// code value c holds eight 16-byte copies of C_0[c] (slots 0..7) and eight of
+// C_1[c] (slots 8..15); lane r of a 16-lane LDS pass reads slot r first
+// (codebook r / 8) and slot r ^ 8 second, so every pass touches all 64 banks
+// once whatever the codes. The fp16 sum does not depend on the order of its
+// two terms. After the K loop the same LDS holds the partial tiles.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -68,8 +75,11 @@ struct MidCfg {
 // B-ring depth: enough steps ahead to cover ~1000 clocks of MFMA work.
 constexpr int ring_depth(int rt, int nt) { return rt * nt >= 16 ? 2 : rt * nt >= 8 ? 4 : 8; }
 
+// LDS: the 2x8 table (reused for the partial tiles after the K loop), then
+// the row scales
+constexpr size_t mid_red_bytes(int rt, int nt) { return (size_t)kMidWaves * rt * nt * 1024; }
 constexpr size_t mid_lds_bytes(bool lut, int rt, int nt) {
-  return (lut ? 8192 : 0) + (size_t)kMidWaves * rt * nt * 1024;
+  return ((lut && mid_red_bytes(rt, nt) < 65536) ? 65536 : mid_red_bytes(rt, nt)) + 64 * 4;
 }
 
 // Code of step s (a compile-time constant) from a lane's 16 code bytes: g = 8
@@ -158,8 +168,9 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   constexpr int D = ring_depth(RT, NT);
   static_assert(STEPS % D == 0, "the ring depth divides the steps of a super-chunk");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint4 *lds_books = reinterpret_cast<uint4 *>(lds);
-  float4_t *red = reinterpret_cast<float4_t *>(lds + (LUT ? 8192 : 0));
+  uint8_t *table = lds;
+  float4_t *red = reinterpret_cast<float4_t *>(lds);
+  float *lds_scale = reinterpret_cast<float *>(lds + mid_lds_bytes(LUT, RT, NT) - 64 * 4);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,6 +183,9 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   const Rsrc crs = make_rsrc(codes, codes_bytes);
   const Rsrc xrs = make_rsrc(xb, xb_bytes);
   const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
+
+  // the row scales for the epilogue (read after the barriers that end the K loop)
+  if (tid < 16 * RT) lds_scale[tid] = row0 + tid < out ? h2f(scales[row0 + tid]) : 0.0f;
 
   const uint32_t code_lane = (uint32_t)(row0 + r) * row_bytes + (uint32_t)q * 16u;
   const uint32_t x_lane = ((uint32_t)(q * G * BP) + (uint32_t)r) * 16u;
@@ -200,12 +214,22 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
       ga[t] = gbooks[G == 8 ? code : 2u * code + (uint32_t)(s & 1)];
     }
   };
-  // 2x8: the fp16 sum of the two codewords of step s
+  // 2x8: the fp16 sum of the two codewords of step s. A table address is
+  // (code << 8) | (slot * 16): one byte permute per read picks the code byte
+  // of this lane's codebook (r / 8 first, the other second).
+  const uint32_t baseA = (uint32_t)r * 16u, baseB = (uint32_t)(r ^ 8) * 16u;
+  const uint32_t mA = (uint32_t)(r >> 3), mB = mA ^ 1u;
+  const uint32_t selA[2] = {0x0C0C0000u | ((4u + mA) << 8), 0x0C0C0000u | ((6u + mA) << 8)};
+  const uint32_t selB[2] = {0x0C0C0000u | ((4u + mB) << 8), 0x0C0C0000u | ((6u + mB) << 8)};
   auto decode = [&](const uint4 (&cw)[RT], int s, uint4 (&a)[RT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const uint32_t code = code_of<G>(cw[t], s);
-      a[t] = hadd8(lds_books[code & 0xFFu], lds_books[256u + (code >> 8)]);
+      const uint32_t word = (s >> 1) == 0 ? cw[t].x : (s >> 1) == 1 ? cw[t].y
+                          : (s >> 1) == 2 ? cw[t].z : cw[t].w;
+      const uint32_t addrA = __builtin_amdgcn_perm(word, baseA, selA[s & 1]);
+      const uint32_t addrB = __builtin_amdgcn_perm(word, baseB, selB[s & 1]);
+      a[t] = hadd8(*reinterpret_cast<const uint4 *>(table + addrA),
+                   *reinterpret_cast<const uint4 *>(table + addrB));
     }
   };
 
@@ -225,7 +249,18 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
 #pragma unroll
   for (int i = 0; i < D; ++i) load_x(sc, i, bx[i]);
   if constexpr (LUT) {
-    for (int i = tid; i < 512; i += kMidThreads) lds_books[i] = gbooks[i];
+    // each thread writes the 8 copies of two codewords, copy (j + tid) % 8 in
+    // write j: the 16 lanes of a pass hit 16 distinct slots (lanes 8 apart
+    // hold the two codebooks)
+    const int tm = (tid >> 3) & 1;
+    const int tc = (tid & 7) | ((tid >> 4) << 3);
+    const uint4 v0 = gbooks[tm * 256 + tc], v1 = gbooks[tm * 256 + tc + 128];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int slot = ((j + tid) & 7) * 16;
+      *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + slot) = v0;
+      *reinterpret_cast<uint4 *>(table + (tc + 128) * 256 + tm * 128 + slot) = v1;
+    }
     __syncthreads();
     decode(cw[0], 0, a[0]);
   } else {
@@ -274,7 +309,9 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
     super_chunk(std::integral_constant<int, 1>{});
   }
 
-  // the four wavefronts' partial tiles, added in wavefront order
+  // the four wavefronts' partial tiles, added in wavefront order (the 2x8
+  // table is dead once every wavefront has left the K loop)
+  if constexpr (LUT) __syncthreads();
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -288,8 +325,27 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
     return v;
   };
   if (splits == 1) {
-    for (int e = tid; e < E; e += kMidThreads)
-      store_out<NT>(y, scales, out, batch, row0, e, wave_sum(e));
+    for (int e = tid; e < E; e += kMidThreads) {
+      const float4_t v = wave_sum(e);
+      const int tj = e >> 6, l = e & 63;
+      const int t = tj / NT, j = tj - t * NT;
+      const int tok = j * 16 + (l & 15);
+      if (tok >= batch) continue;
+      const int rr = t * 16 + 4 * (l >> 4);
+      const int row = row0 + rr;
+      uint16_t *dst = y + (int64_t)tok * out + row;
+      const float s0 = lds_scale[rr], s1 = lds_scale[rr + 1];
+      const float s2 = lds_scale[rr + 2], s3 = lds_scale[rr + 3];
+      if ((out & 3) == 0 && row + 3 < out) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(f2h(v[0] * s0) | (f2h(v[1] * s1) << 16),
+                                                     f2h(v[2] * s2) | (f2h(v[3] * s3) << 16));
+      } else {
+        const float sv[4] = {s0, s1, s2, s3};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (row + k < out) dst[k] = (uint16_t)f2h(v[k] * sv[k]);
+      }
+    }
   } else {
     float4_t *mine = part + ((size_t)rb * splits + sp) * E;
     for (int e = tid; e < E; e += kMidThreads) mine[e] = wave_sum(e);
