@@ -17,11 +17,17 @@
 //   * dequant: the sum times the row scale in float32, one round to float16;
 //   * GEMV (1..8 activation rows): float32 dot of the sum with x, scale once
 //     per row, wavefront reduction in a fixed order;
-//   * GEMM (any batch): each 64 x 64 weight tile is decoded exactly as in
-//     dequant into LDS, then multiplied with the activation tile on the
-//     matrix cores (v_mfma_f32_32x32x16_f16, float32 accumulation), i.e. the
-//     product of x with the float16 weights that dequant would write.
+//   * GEMM: the product of x with the float16 weights that dequant would
+//     write, on the matrix cores with float32 accumulation. Up to 32
+//     activation rows, each lane decodes its 8 weights of an MFMA step
+//     exactly into the A operand of v_mfma_f32_16x16x32_f16 (workgroups of 16
+//     output rows, wavefronts interleaved over K, codes and codewords loaded
+//     two and one steps ahead); above, each 64 x 64 weight tile is decoded
+//     into LDS and multiplied with the staged activation tile
+//     (v_mfma_f32_32x32x16_f16).
 // Codebooks are read through the cache hierarchy (8 KiB to 16 MiB).
+#include <type_traits>
+
 #include "aqlm_device.hpp"
 
 namespace aqlm {
@@ -249,6 +255,148 @@ __global__ __launch_bounds__(kGenBlock) void gemm_general_kernel(
   }
 }
 
+// Up to 32 activation rows (NT tiles of 16): a workgroup of kGenSkWaves
+// wavefronts owns 16 output rows; wavefront w takes the K blocks of 32 inputs
+// w, w + kGenSkWaves, ... In MFMA step kb, lane (r, q) = (lane % 16, lane / 16)
+// decodes weights 8q .. 8q+7 of K block kb of row r exactly (the M codewords,
+// or their halves for g = 16, summed in float32 in ascending m, times the row
+// scale, one round) into the A operand, and loads the matching 16 bytes of
+// activation row 16 j + r as the B operand of tile j. The wavefronts' float32
+// tiles are added in LDS in wavefront order. Codes are loaded two steps ahead
+// and codewords and activations one step ahead, from registers rings indexed
+// statically (the step loop is unrolled by two).
+constexpr int kGenSkWaves = 8;
+constexpr int kGenMaxM = 8;
+
+template <int G, int CB, int NT>
+__global__ __launch_bounds__(64 * kGenSkWaves) void gemm_general_skinny_kernel(
+    Codes codes, const uint16_t *__restrict__ books, const uint16_t *__restrict__ scales,
+    const uint16_t *__restrict__ x, uint16_t *__restrict__ y, int out, int in, int groups,
+    int batch, int M, int B) {
+  __shared__ float4_t red[kGenSkWaves * NT * 64];
+  const uint4 *gb = reinterpret_cast<const uint4 *>(books);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int row = blockIdx.x * 16 + r;
+  const bool row_ok = row < out;
+  const int nkb = (in + 31) / 32;
+  const float s = row_ok ? h2f(scales[row]) : 0.0f;
+  const Rsrc xr = make_rsrc(x, (uint32_t)((int64_t)batch * in * 2));
+  constexpr uint32_t kOOB = 0x80000000u;
+
+  // group and codeword part (g = 16: which half) of this lane in K block kb
+  auto group_of = [&](int kb) { return G == 8 ? kb * 4 + q : kb * 2 + (q >> 1); };
+  constexpr int kHalfOff = G == 8 ? 0 : 1;  // uint4 index step of the second half
+  auto load_codes = [&](int kb, uint32_t (&c)[kGenMaxM]) __attribute__((always_inline)) {
+    const int j = group_of(kb);
+    const bool ok = row_ok && kb < nkb && j < groups;
+#pragma unroll
+    for (int m = 0; m < kGenMaxM; ++m)
+      c[m] = (ok && m < M) ? code_at<CB>(codes, (int64_t)row * groups + j, M, B, m) : 0u;
+  };
+  auto load_words = [&](const uint32_t (&c)[kGenMaxM], uint4 (&cw)[kGenMaxM])
+                        __attribute__((always_inline)) {
+    const int half = G == 8 ? 0 : (q & 1);
+#pragma unroll
+    for (int m = 0; m < kGenMaxM; ++m)
+      if (m < M)
+        cw[m] = gb[(((size_t)m << B) + c[m]) * (G / 8) + (size_t)(half * kHalfOff)];
+  };
+  auto load_x = [&](int kb, uint4 (&bx)[NT]) __attribute__((always_inline)) {
+    const int col = kb * 32 + 8 * q;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int tok = j * 16 + r;
+      const bool ok = kb < nkb && tok < batch && col < in;
+      bx[j] = buf_load16(xr, ok ? (uint32_t)(((int64_t)tok * in + col) * 2) : kOOB);
+    }
+  };
+  // the exact float16 weights of this lane's 8 inputs (zero past the row end)
+  auto decode = [&](int kb, const uint4 (&cw)[kGenMaxM]) __attribute__((always_inline)) {
+    float acc[8];
+    {
+      const uint32_t wd[4] = {cw[0].x, cw[0].y, cw[0].z, cw[0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = h2f(wd[i] & 0xFFFFu);
+        acc[2 * i + 1] = h2f(wd[i] >> 16);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < kGenMaxM; ++m) {
+      if (m < M) {
+        const uint32_t wd[4] = {cw[m].x, cw[m].y, cw[m].z, cw[m].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = materialize(acc[2 * i] + h2f(wd[i] & 0xFFFFu));
+          acc[2 * i + 1] = materialize(acc[2 * i + 1] + h2f(wd[i] >> 16));
+        }
+      }
+    }
+    const bool ok = row_ok && kb < nkb && group_of(kb) < groups;
+    uint32_t words[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = f2h(materialize(materialize(acc[2 * i]) * s));
+      const uint32_t hi = f2h(materialize(materialize(acc[2 * i + 1]) * s));
+      words[i] = ok ? (lo | (hi << 16)) : 0u;
+    }
+    return make_uint4(words[0], words[1], words[2], words[3]);
+  };
+
+  float4_t acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t c[2][kGenMaxM];
+  uint4 cw[2][kGenMaxM];
+  uint4 bx[2][NT];
+  int kb = w;
+  constexpr int KS = kGenSkWaves;
+  load_codes(kb, c[0]);
+  load_codes(kb + KS, c[1]);
+  load_words(c[0], cw[0]);
+  load_x(kb, bx[0]);
+  // step kb with ring slot K: codewords and activations of the next step,
+  // codes of the step after it, then decode and multiply
+  auto step = [&](auto kc) __attribute__((always_inline)) {
+    constexpr int K = decltype(kc)::value;
+    load_words(c[K ^ 1], cw[K ^ 1]);
+    load_x(kb + KS, bx[K ^ 1]);
+    load_codes(kb + 2 * KS, c[K]);
+    const uint4 a = decode(kb, cw[K]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                     __builtin_bit_cast(half8_t, bx[K][j]), acc[j],
+                                                     0, 0, 0);
+    kb += KS;
+  };
+  while (kb < nkb) {
+    step(std::integral_constant<int, 0>{});
+    if (kb >= nkb) break;
+    step(std::integral_constant<int, 1>{});
+  }
+
+#pragma unroll
+  for (int j = 0; j < NT; ++j) red[(w * NT + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  // element e = tile j * 64 + lane l: rows 4 (l / 16) .. + 3, activation row 16 j + l % 16
+  for (int e = tid; e < NT * 64; e += 64 * kGenSkWaves) {
+    float4_t v = red[e];
+#pragma unroll
+    for (int w2 = 1; w2 < kGenSkWaves; ++w2) v += red[w2 * NT * 64 + e];
+    const int j = e >> 6, l = e & 63;
+    const int tok = j * 16 + (l & 15);
+    if (tok >= batch) continue;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = blockIdx.x * 16 + 4 * (l >> 4) + k;
+      if (rr < out) y[(int64_t)tok * out + rr] = (uint16_t)f2h(v[k]);
+    }
+  }
+}
+
 Codes codes_of(const LayerDesc &L) {
   const uint8_t *p = static_cast<const uint8_t *>(L.codes);
   const uint32_t bytes = L.packed ? packed_stream_bytes(L.out * L.groups * L.M, L.B) : 0u;
@@ -299,6 +447,18 @@ hipError_t gemv_g(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
 template <int G, int CB>
 hipError_t gemm_gc(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                    hipStream_t stream) {
+  if (batch <= 32 && L.M <= kGenMaxM && L.in * batch * 2 < ((int64_t)1 << 31)) {
+    const dim3 g((unsigned)((L.out + 15) / 16));
+    if (batch <= 16)
+      hipLaunchKernelGGL((gemm_general_skinny_kernel<G, CB, 1>), g, dim3(64 * kGenSkWaves), 0,
+                         stream, codes_of(L), L.books, L.scales, x, y, (int)L.out, (int)L.in,
+                         (int)L.groups, (int)batch, L.M, L.B);
+    else
+      hipLaunchKernelGGL((gemm_general_skinny_kernel<G, CB, 2>), g, dim3(64 * kGenSkWaves), 0,
+                         stream, codes_of(L), L.books, L.scales, x, y, (int)L.out, (int)L.in,
+                         (int)L.groups, (int)batch, L.M, L.B);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((L.out + kGenTile - 1) / kGenTile),
                   (unsigned)((batch + kGenTile - 1) / kGenTile));
   hipLaunchKernelGGL((gemm_general_kernel<G, CB>), grid, dim3(kGenBlock), 0, stream,

@@ -42,7 +42,7 @@ def test_general_small(scheme, out, J):
         y_ref, bound = oracle.product(x[:batch], w_ref)
         assert_product(layer.gemv(dev_x(x[:batch])), y_ref, bound,
                        f"gemv {scheme.name} {out}x{J} b{batch}")
-    for batch in (1, 9, 64, 70):
+    for batch in (1, 9, 20, 32, 33, 64, 70):
         y_ref, bound = oracle.product(x[:batch], w_ref)
         assert_product(layer.gemm(dev_x(x[:batch])), y_ref, bound,
                        f"gemm {scheme.name} {out}x{J} b{batch}")
