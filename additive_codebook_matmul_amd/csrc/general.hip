@@ -18,7 +18,7 @@
 //   * GEMV (1..8 activation rows): float32 dot of the sum with x, scale once
 //     per row, wavefront reduction in a fixed order;
 //   * GEMM: the product of x with the float16 weights that dequant would
-//     write, on the matrix cores with float32 accumulation. Up to 32
+//     write, on the matrix cores with float32 accumulation. Up to 128
 //     activation rows, each lane decodes its 8 weights of an MFMA step
 //     exactly into the A operand of v_mfma_f32_16x16x32_f16 (workgroups of 16
 //     output rows, wavefronts interleaved over K, codes and codewords loaded
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kGenBlock) void gemm_general_kernel(
   }
 }
 
-// Up to 32 activation rows (NT tiles of 16): a workgroup of kGenSkWaves
+// Up to 128 activation rows (NT tiles of 16): a workgroup of kGenSkWaves
 // wavefronts owns 16 output rows; wavefront w takes the K blocks of 32 inputs
 // w, w + kGenSkWaves, ... In MFMA step kb, lane (r, q) = (lane % 16, lane / 16)
 // decodes weights 8q .. 8q+7 of K block kb of row r exactly (the M codewords,
@@ -267,6 +267,7 @@ __global__ __launch_bounds__(kGenBlock) void gemm_general_kernel(
 // statically (the step loop is unrolled by two).
 constexpr int kGenSkWaves = 8;
 constexpr int kGenMaxM = 8;
+constexpr int kGenSkMaxTiles = 8;  // up to 128 activation rows
 
 template <int G, int CB, int NT>
 __global__ __launch_bounds__(64 * kGenSkWaves) void gemm_general_skinny_kernel(
@@ -447,16 +448,18 @@ hipError_t gemv_g(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
 template <int G, int CB>
 hipError_t gemm_gc(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                    hipStream_t stream) {
-  if (batch <= 32 && L.M <= kGenMaxM && L.in * batch * 2 < ((int64_t)1 << 31)) {
+  // bit-packed codes keep a two-word window per code in flight: at most four
+  // activation tiles fit in registers
+  constexpr int kMaxTiles = CB == 0 ? 4 : kGenSkMaxTiles;
+  if (batch <= 16 * kMaxTiles && L.M <= kGenMaxM && L.in * batch * 2 < ((int64_t)1 << 31)) {
     const dim3 g((unsigned)((L.out + 15) / 16));
-    if (batch <= 16)
-      hipLaunchKernelGGL((gemm_general_skinny_kernel<G, CB, 1>), g, dim3(64 * kGenSkWaves), 0,
-                         stream, codes_of(L), L.books, L.scales, x, y, (int)L.out, (int)L.in,
-                         (int)L.groups, (int)batch, L.M, L.B);
-    else
-      hipLaunchKernelGGL((gemm_general_skinny_kernel<G, CB, 2>), g, dim3(64 * kGenSkWaves), 0,
-                         stream, codes_of(L), L.books, L.scales, x, y, (int)L.out, (int)L.in,
-                         (int)L.groups, (int)batch, L.M, L.B);
+    auto k = batch <= 16   ? gemm_general_skinny_kernel<G, CB, 1>
+             : batch <= 32 ? gemm_general_skinny_kernel<G, CB, 2>
+                           : gemm_general_skinny_kernel<G, CB, 4>;
+    if constexpr (kMaxTiles == 8)
+      if (batch > 64) k = gemm_general_skinny_kernel<G, CB, 8>;
+    hipLaunchKernelGGL(k, g, dim3(64 * kGenSkWaves), 0, stream, codes_of(L), L.books, L.scales, x,
+                       y, (int)L.out, (int)L.in, (int)L.groups, (int)batch, L.M, L.B);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((L.out + kGenTile - 1) / kGenTile),
