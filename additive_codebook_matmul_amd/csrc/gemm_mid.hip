@@ -1,4 +1,4 @@
-// Batched product y = x . W^T for 17..128 activation rows with a caller-owned
+// Batched product y = x . W^T for 17 and more activation rows with a caller-owned
 // device workspace (aqlm_gemm_ws). The weights are decoded on chip straight
 // into the A operand of v_mfma_f32_16x16x32_f16 (float32 accumulation) and
 // are never written to memory.
@@ -60,7 +60,7 @@ constexpr int kMidThreads = 64 * kMidWaves;
 constexpr int kGroupsPerSc = 32;  // groups per super-chunk
 constexpr uint32_t kMidOOB = 0x80000000u;
 constexpr int64_t kMidMinBatch = 17;  // up to 16 rows the skinny kernel of aqlm_gemm is as fast
-constexpr int64_t kMidMaxBatch = 128;
+constexpr int64_t kMidMaxBatch = 4096;
 constexpr int kMidCus = 256;
 constexpr int kMidOccupancy = 1;  // wavefronts per SIMD the kernel is built for
 constexpr int kMidMaxTiles = 32;  // largest RT * NT (accumulator tiles per wavefront)
@@ -144,13 +144,14 @@ __global__ __launch_bounds__(256) void gemm_mid_reduce_kernel(const float4_t *__
                                                               uint16_t *__restrict__ y, int out,
                                                               int batch, int splits) {
   constexpr int E = RT * NT * 64;
-  const int rb = blockIdx.y;
+  const int rb = blockIdx.y, tb = blockIdx.z;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= E) return;
-  const float4_t *p = part + (size_t)rb * splits * E + e;
+  const float4_t *p = part + ((size_t)tb * gridDim.y + rb) * splits * E + e;
   float4_t v = p[0];
   for (int k = 1; k < splits; ++k) v += p[(size_t)k * E];
-  store_out<NT>(y, scales, out, batch, rb * 16 * RT, e, v);
+  const int tok0 = tb * 16 * NT;
+  store_out<NT>(y + (int64_t)tok0 * out, scales, out, batch - tok0, rb * 16 * RT, e, v);
 }
 
 template <Scheme S, int RT, int NT>
@@ -159,11 +160,10 @@ __attribute__((amdgpu_waves_per_eu(kMidOccupancy, kMidOccupancy)))
 void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
                      const uint16_t *__restrict__ scales, const uint4 *__restrict__ xb,
                      uint16_t *__restrict__ y, float4_t *__restrict__ part, int out, int groups,
-                     int batch, int splits, uint32_t codes_bytes, uint32_t xb_bytes) {
+                     int batch, int splits, int bp, uint32_t codes_bytes, uint32_t xb_bytes) {
   using C = MidCfg<S>;
   constexpr int G = C::G, STEPS = C::STEPS;
   constexpr bool LUT = S == Scheme::k2x8;
-  constexpr int BP = 16 * NT;
   constexpr int E = RT * NT * 64;  // float4 accumulators of a workgroup tile
   constexpr int D = ring_depth(RT, NT);
   static_assert(STEPS % D == 0, "the ring depth divides the steps of a super-chunk");
@@ -176,6 +176,9 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int sp = (int)(blockIdx.x % (unsigned)splits), rb = (int)(blockIdx.x / (unsigned)splits);
+  // activation block: rows tok0 .. tok0 + 16 NT - 1 of the batch (of bp rows in xb)
+  const int tok0 = blockIdx.y * 16 * NT;
+  const int nb = batch - tok0;
   const int row0 = rb * 16 * RT;
   const int nsc = (groups + kGroupsPerSc - 1) / kGroupsPerSc;
   const int sc_end = (int)((int64_t)(sp + 1) * nsc / splits);
@@ -188,9 +191,9 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   if (tid < 16 * RT) lds_scale[tid] = row0 + tid < out ? h2f(scales[row0 + tid]) : 0.0f;
 
   const uint32_t code_lane = (uint32_t)(row0 + r) * row_bytes + (uint32_t)q * 16u;
-  const uint32_t x_lane = ((uint32_t)(q * G * BP) + (uint32_t)r) * 16u;
-  constexpr uint32_t kBlockBytes = BP * 16u;  // one k-block of xb
-  constexpr uint32_t kScXBytes = C::SC_BLOCKS * kBlockBytes;
+  const uint32_t x_lane = ((uint32_t)(q * G * bp) + (uint32_t)(tok0 + r)) * 16u;
+  const uint32_t kBlockBytes = (uint32_t)bp * 16u;  // one k-block of xb
+  const uint32_t kScXBytes = (uint32_t)C::SC_BLOCKS * kBlockBytes;
 
   // this lane's 16 code bytes of super-chunk sc for every row tile
   auto load_codes = [&](int sc, uint4 (&cw)[RT]) __attribute__((always_inline)) {
@@ -330,10 +333,10 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
       const int tj = e >> 6, l = e & 63;
       const int t = tj / NT, j = tj - t * NT;
       const int tok = j * 16 + (l & 15);
-      if (tok >= batch) continue;
+      if (tok >= nb) continue;
       const int rr = t * 16 + 4 * (l >> 4);
       const int row = row0 + rr;
-      uint16_t *dst = y + (int64_t)tok * out + row;
+      uint16_t *dst = y + (int64_t)(tok0 + tok) * out + row;
       const float s0 = lds_scale[rr], s1 = lds_scale[rr + 1];
       const float s2 = lds_scale[rr + 2], s3 = lds_scale[rr + 3];
       if ((out & 3) == 0 && row + 3 < out) {
@@ -347,7 +350,7 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
       }
     }
   } else {
-    float4_t *mine = part + ((size_t)rb * splits + sp) * E;
+    float4_t *mine = part + ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * E;
     for (int e = tid; e < E; e += kMidThreads) mine[e] = wave_sum(e);
   }
 }
@@ -359,7 +362,7 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
 // LDS codebook reads (2x8) or L2 codeword gathers (1x16) -- times the steps
 // per wavefront, times the rounds of workgroups over the CUs.
 struct MidPlan {
-  int nt = 0, rt = 0, splits = 0, nrb = 0;
+  int nt = 0, ntb = 0, rt = 0, splits = 0, nrb = 0;
   size_t xb_bytes = 0, part_off = 0, total = 0;
 };
 
@@ -370,14 +373,28 @@ int mid_nt(int64_t batch) {
   return n <= 4 ? n : n <= 6 ? 6 : 8;
 }
 
+// Above 128 rows the wide tiles (256 output rows x 64 or 128 activation
+// rows per workgroup, no split of K) take over once their grid gives most
+// CUs a workgroup (measured on 11008 x 4096 and 4096 x 11008 layers, 129 to
+// 2048 rows); below that the 128-row blocks of this kernel, with K split as
+// needed, keep every CU busy.
+bool mid_beats_wide(const LayerDesc &L, int64_t batch) {
+  const int64_t wide_rows = L.scheme == Scheme::k2x8 ? 64 : 128;
+  const int64_t wide_blocks = ((L.out + 255) / 256) * ((batch + wide_rows - 1) / wide_rows);
+  return wide_blocks < kMidCus * 5 / 8;
+}
+
 bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
   if (L.scheme == Scheme::kGeneral || L.packed || batch < kMidMinBatch || batch > kMidMaxBatch)
     return false;
   if (L.groups % 8 != 0) return false;  // a lane's 16 code bytes never straddle a row end
   const int G = group_size(L.scheme);
   const int steps = G;
-  const int nt = mid_nt(batch);
-  const int64_t bp = 16 * nt;
+  // above 128 rows: blocks of 128 activation rows, one more grid dimension
+  const int nt = batch <= 128 ? mid_nt(batch) : 8;
+  const int ntb = (int)((batch + 16 * nt - 1) / (16 * nt));
+  if (batch > 128 && !mid_beats_wide(L, batch)) return false;
+  const int64_t bp = 16 * nt * ntb;
   const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
   const int64_t nsc = (L.groups + kGroupsPerSc - 1) / kGroupsPerSc;
   const int64_t xb_bytes = L.in * bp * 2;
@@ -397,11 +414,13 @@ bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
       const int64_t sc_per_wave = ((nsc + splits - 1) / splits + kMidWaves - 1) / kMidWaves;
       const double wg = sc_per_wave * steps * round +
                         (splits > 1 ? 2000.0 + 16.0 * rt * nt : 0.0);
-      const int64_t rounds = (nrb * splits + kMidCus * kMidOccupancy - 1) / (kMidCus * kMidOccupancy);
+      const int64_t rounds =
+          (nrb * splits * ntb + kMidCus * kMidOccupancy - 1) / (kMidCus * kMidOccupancy);
       const double t = rounds * wg;
       if (p->nt == 0 || t < best) {
         best = t;
         p->nt = nt;
+        p->ntb = ntb;
         p->rt = rt;
         p->splits = splits;
         p->nrb = (int)nrb;
@@ -411,7 +430,8 @@ bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
   if (p->nt == 0) return false;
   p->xb_bytes = (size_t)xb_bytes;
   p->part_off = align256((size_t)xb_bytes);
-  p->total = p->part_off + (p->splits > 1 ? (size_t)p->nrb * p->splits * p->rt * p->nt * 1024 : 0);
+  p->total = p->part_off +
+             (p->splits > 1 ? (size_t)p->nrb * p->splits * p->ntb * p->rt * p->nt * 1024 : 0);
   return p->total < (size_t(1) << 40);
 }
 
@@ -439,21 +459,22 @@ hipError_t launch_mid_t(const LayerDesc &L, const MidPlan &P, const uint16_t *x,
   uint4 *xb = reinterpret_cast<uint4 *>(ws);
   float4_t *part = reinterpret_cast<float4_t *>(ws + P.part_off);
   const int nkb = (int)(L.in / 8);
-  hipLaunchKernelGGL(gemm_xblock_kernel, dim3((unsigned)((nkb + 15) / 16), (unsigned)NT),
+  const int bp = 16 * NT * P.ntb;
+  hipLaunchKernelGGL(gemm_xblock_kernel, dim3((unsigned)((nkb + 15) / 16), (unsigned)(bp / 16)),
                      dim3(256), 0, stream, reinterpret_cast<const uint4 *>(x), xb, nkb, (int)batch,
-                     16 * NT);
+                     bp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)(P.nrb * P.splits)), dim3(kMidThreads), lds, stream,
-                     static_cast<const uint8_t *>(L.codes), L.books, L.scales, xb, y, part,
-                     (int)L.out, (int)L.groups, (int)batch, P.splits,
+  hipLaunchKernelGGL(k, dim3((unsigned)(P.nrb * P.splits), (unsigned)P.ntb), dim3(kMidThreads), lds,
+                     stream, static_cast<const uint8_t *>(L.codes), L.books, L.scales, xb, y, part,
+                     (int)L.out, (int)L.groups, (int)batch, P.splits, bp,
                      (uint32_t)(L.out * L.groups * kCodeBytesPerGroup), (uint32_t)P.xb_bytes);
   e = hipGetLastError();
   if (e != hipSuccess || P.splits == 1) return e;
   constexpr int E = RT * NT * 64;
-  hipLaunchKernelGGL((gemm_mid_reduce_kernel<RT, NT>), dim3((unsigned)((E + 255) / 256),
-                     (unsigned)P.nrb), dim3(256), 0, stream, part, L.scales, y, (int)L.out,
-                     (int)batch, P.splits);
+  hipLaunchKernelGGL((gemm_mid_reduce_kernel<RT, NT>),
+                     dim3((unsigned)((E + 255) / 256), (unsigned)P.nrb, (unsigned)P.ntb), dim3(256),
+                     0, stream, part, L.scales, y, (int)L.out, (int)batch, P.splits);
   return hipGetLastError();
 }
 

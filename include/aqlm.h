@@ -145,13 +145,14 @@ AQLM_API int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, in
 
 /*
  * aqlm_gemm_ws: the product of aqlm_gemm with a caller-owned device
- * workspace, which lets batches of 17..128 activation rows of the three
- * dedicated schemes (2x8, 1x16 and 1x16 with g = 16; element codes, in / g a
- * multiple of 8) run the workspace form of the matrix-core path: the
- * activations are first re-laid into blocks of 8 inputs so that every MFMA
- * operand load is contiguous, and K may be split across workgroups whose
- * float32 partial sums meet in the workspace. Every other case runs as
- * aqlm_gemm and ignores the workspace.
+ * workspace, which lets the three dedicated schemes (2x8, 1x16 and 1x16 with
+ * g = 16; element codes, in / g a multiple of 8) run the workspace form of
+ * the matrix-core path from 17 activation rows up to the batch where the
+ * wide tiles of aqlm_gemm fill the chip by themselves (at most 4096 rows):
+ * the activations are first re-laid into blocks of 8 inputs so that every
+ * MFMA operand load is contiguous, rows beyond 128 go to blocks of 128, and
+ * K may be split across workgroups whose float32 partial sums meet in the
+ * workspace. Every other case runs as aqlm_gemm and ignores the workspace.
  *   workspace        device pointer, 16-byte aligned, at least
  *                    aqlm_gemm_workspace_size bytes (NULL allowed when that
  *                    size is 0); overwritten by the call; must not overlap

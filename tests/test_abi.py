@@ -128,7 +128,8 @@ def _ws_size(s, batch):
 
 
 def test_workspace_size():
-    """Host-side sizing: the workspace form covers 17..128 rows of the three
+    """Host-side sizing: the workspace form covers 17 rows and up (while the
+    wide tiles' grid is small) of the three
     dedicated schemes with element codes and in/g a multiple of 8; it holds at
     least the re-laid activations (in x 16*ceil(batch/16) float16 values)."""
     mlp = dict(out=4096, n_in=11008)
@@ -140,7 +141,9 @@ def test_workspace_size():
             assert n % 16 == 0
     assert _ws_size(_layer(**mlp), 0) == (0, 0)
     assert _ws_size(_layer(**mlp), 16) == (0, 0)                     # skinny tiles need none
-    assert _ws_size(_layer(**mlp), 129) == (0, 0)                    # wide tiles need none
+    assert _ws_size(_layer(**mlp), 129)[1] > 0                       # two blocks of 128 rows
+    assert _ws_size(_layer(**mlp), 4096) == (0, 0)                   # the wide tiles fill the chip
+    assert _ws_size(_layer(out=11008, n_in=4096), 1024) == (0, 0)
     assert _ws_size(_layer(3, 8, 8, **mlp), 64) == (0, 0)            # general scheme
     assert _ws_size(_layer(flags=1, **mlp), 64) == (0, 0)            # bit-packed codes
     assert _ws_size(_layer(out=64, n_in=36 * 8), 64) == (0, 0)       # in/g not a multiple of 8

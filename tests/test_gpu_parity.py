@@ -188,11 +188,12 @@ def test_workload_gemv(wname, lname, batch):
         assert_product(y, y_ref, bound, f"{wname}/{lname} b{batch}")
 
 
-# the workload's batches plus batches of the mid-size GEMM (33..128 rows:
+# the workload's batches plus batches of the workspace GEMM (33..128 rows:
 # four row tiles per workgroup at 33/64 on the 11008-row layers, a half
-# chunk at the end of the 11008-input rows)
+# chunk at the end of the 11008-input rows; 200 rows: two blocks of 128
+# activation rows on the layers whose wide grid would be small)
 GEMM_IDS = [(l.name, b) for l in WL.WORKLOADS["gemm_mlp"].layers
-            for b in sorted(set(WL.WORKLOADS["gemm_mlp"].batches) | {33, 64, 100})]
+            for b in sorted(set(WL.WORKLOADS["gemm_mlp"].batches) | {33, 64, 100, 200})]
 
 
 @pytest.mark.parametrize("lname,batch", GEMM_IDS, ids=lambda v: str(v))
