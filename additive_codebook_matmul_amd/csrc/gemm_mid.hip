@@ -30,9 +30,10 @@
 // third launch (gemm_mid_reduce_kernel) adds the parts of each output in part
 // order, scales and writes y: deterministic, and free of cross-workgroup
 // synchronisation (a device-scope release inside the kernel would write back
-// the whole L2 of the XCD once per workgroup). With splits dividing 8, part k
-// of every row block runs on XCD k mod 8, so each XCD's L2 holds only its
-// share of xb.
+// the whole L2 of the XCD once per workgroup). Workgroups are dispatched to
+// the XCDs in turn, so with splits dividing 8 the parts of one block of
+// activation rows land on fixed XCDs and each XCD's L2 holds only its share
+// of xb.
 //
 // Pipelining: codes one super-chunk ahead; B operands (and the 1x16 codewords,
 // gathered from the L2-resident codebook) D steps ahead in register rings; the
