@@ -8,10 +8,10 @@
 // rows. Loaded straight from x [batch][in], every lane of a wavefront touches
 // its own cache line and the vector L1 serves about one lane per clock. The
 // first launch (gemm_xblock_kernel) therefore re-lays x into k-blocks of 8
-// inputs,
-//   xb[kb][t][0..7] = x[t][8 kb .. 8 kb + 7]    (t < BP = 16 NT, zero past batch),
+// inputs, one slab per block of BP = 16 NT activation rows,
+//   xb[tb][kb][t][0..7] = x[tb BP + t][8 kb .. 8 kb + 7]    (zero past batch),
 // after which the B operand of one MFMA step for 16 activation rows is one
-// contiguous 256-byte run. The workspace also holds the float32 partial tiles
+// contiguous 256-byte run, and the k-block stride is a compile-time constant. The workspace also holds the float32 partial tiles
 // of the split-K form below.
 //
 // Tiles. A workgroup of four wavefronts owns RT tiles of 16 output rows and
@@ -95,7 +95,7 @@ __device__ __forceinline__ uint32_t code_of(const uint4 &cw, int s) {
 
 __global__ __launch_bounds__(256) void gemm_xblock_kernel(const uint4 *__restrict__ x,
                                                           uint4 *__restrict__ xb, int nkb,
-                                                          int batch, int bp) {
+                                                          int batch, int bp_block) {
   // 16 activation rows x 16 k-blocks through LDS: rows are read and k-blocks
   // written as 256-byte runs (the +1 column keeps the transposed read free of
   // bank conflicts)
@@ -110,8 +110,10 @@ __global__ __launch_bounds__(256) void gemm_xblock_kernel(const uint4 *__restric
   }
   __syncthreads();
   {
-    const int kb = kb0 + (i >> 4), t = t0 + (i & 15);
-    if (kb < nkb) xb[(size_t)kb * bp + t] = tile[i & 15][i >> 4];
+    // t0 and bp_block are multiples of 16: the 16 rows share one slab
+    const int tb = t0 / bp_block, t = t0 - tb * bp_block + (i & 15);
+    const int kb = kb0 + (i >> 4);
+    if (kb < nkb) xb[((size_t)tb * nkb + kb) * bp_block + t] = tile[i & 15][i >> 4];
   }
 }
 
@@ -161,10 +163,11 @@ __attribute__((amdgpu_waves_per_eu(kMidOccupancy, kMidOccupancy)))
 void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ books,
                      const uint16_t *__restrict__ scales, const uint4 *__restrict__ xb,
                      uint16_t *__restrict__ y, float4_t *__restrict__ part, int out, int groups,
-                     int batch, int splits, int bp, uint32_t codes_bytes, uint32_t xb_bytes) {
+                     int batch, int splits, uint32_t codes_bytes, uint32_t slab_bytes) {
   using C = MidCfg<S>;
   constexpr int G = C::G, STEPS = C::STEPS;
   constexpr bool LUT = S == Scheme::k2x8;
+  constexpr int BP = 16 * NT;      // activation rows of a workgroup (one slab of xb)
   constexpr int E = RT * NT * 64;  // float4 accumulators of a workgroup tile
   constexpr int D = ring_depth(RT, NT);
   static_assert(STEPS % D == 0, "the ring depth divides the steps of a super-chunk");
@@ -177,24 +180,24 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int sp = (int)(blockIdx.x % (unsigned)splits), rb = (int)(blockIdx.x / (unsigned)splits);
-  // activation block: rows tok0 .. tok0 + 16 NT - 1 of the batch (of bp rows in xb)
-  const int tok0 = blockIdx.y * 16 * NT;
+  // activation block: rows tok0 .. tok0 + BP - 1 of the batch, slab blockIdx.y of xb
+  const int tok0 = blockIdx.y * BP;
   const int nb = batch - tok0;
   const int row0 = rb * 16 * RT;
   const int nsc = (groups + kGroupsPerSc - 1) / kGroupsPerSc;
   const int sc_end = (int)((int64_t)(sp + 1) * nsc / splits);
   const uint32_t row_bytes = (uint32_t)groups * 2u;
   const Rsrc crs = make_rsrc(codes, codes_bytes);
-  const Rsrc xrs = make_rsrc(xb, xb_bytes);
+  const Rsrc xrs = make_rsrc(xb + (size_t)blockIdx.y * (slab_bytes / 16u), slab_bytes);
   const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
 
   // the row scales for the epilogue (read after the barriers that end the K loop)
   if (tid < 16 * RT) lds_scale[tid] = row0 + tid < out ? h2f(scales[row0 + tid]) : 0.0f;
 
   const uint32_t code_lane = (uint32_t)(row0 + r) * row_bytes + (uint32_t)q * 16u;
-  const uint32_t x_lane = ((uint32_t)(q * G * bp) + (uint32_t)(tok0 + r)) * 16u;
-  const uint32_t kBlockBytes = (uint32_t)bp * 16u;  // one k-block of xb
-  const uint32_t kScXBytes = (uint32_t)C::SC_BLOCKS * kBlockBytes;
+  const uint32_t x_lane = ((uint32_t)(q * G * BP) + (uint32_t)r) * 16u;
+  constexpr uint32_t kBlockBytes = BP * 16u;  // one k-block of the slab
+  constexpr uint32_t kScXBytes = C::SC_BLOCKS * kBlockBytes;
 
   // this lane's 16 code bytes of super-chunk sc for every row tile
   auto load_codes = [&](int sc, uint4 (&cw)[RT]) __attribute__((always_inline)) {
@@ -460,16 +463,16 @@ hipError_t launch_mid_t(const LayerDesc &L, const MidPlan &P, const uint16_t *x,
   uint4 *xb = reinterpret_cast<uint4 *>(ws);
   float4_t *part = reinterpret_cast<float4_t *>(ws + P.part_off);
   const int nkb = (int)(L.in / 8);
-  const int bp = 16 * NT * P.ntb;
-  hipLaunchKernelGGL(gemm_xblock_kernel, dim3((unsigned)((nkb + 15) / 16), (unsigned)(bp / 16)),
+  hipLaunchKernelGGL(gemm_xblock_kernel, dim3((unsigned)((nkb + 15) / 16), (unsigned)(NT * P.ntb)),
                      dim3(256), 0, stream, reinterpret_cast<const uint4 *>(x), xb, nkb, (int)batch,
-                     bp);
+                     16 * NT);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3((unsigned)(P.nrb * P.splits), (unsigned)P.ntb), dim3(kMidThreads), lds,
                      stream, static_cast<const uint8_t *>(L.codes), L.books, L.scales, xb, y, part,
-                     (int)L.out, (int)L.groups, (int)batch, P.splits, bp,
-                     (uint32_t)(L.out * L.groups * kCodeBytesPerGroup), (uint32_t)P.xb_bytes);
+                     (int)L.out, (int)L.groups, (int)batch, P.splits,
+                     (uint32_t)(L.out * L.groups * kCodeBytesPerGroup),
+                     (uint32_t)(P.xb_bytes / P.ntb));
   e = hipGetLastError();
   if (e != hipSuccess || P.splits == 1) return e;
   constexpr int E = RT * NT * 64;
