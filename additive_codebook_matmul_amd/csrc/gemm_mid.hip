@@ -14,13 +14,13 @@
 // contiguous 256-byte run, and the k-block stride is a compile-time constant. The workspace also holds the float32 partial tiles
 // of the split-K form below.
 //
-// Tiles. A workgroup of four wavefronts owns RT tiles of 16 output rows and
-// all BP activation rows (NT tiles of 16): each decoded A operand feeds NT
-// MFMAs and each B operand RT MFMAs. K is walked in super-chunks of 32 groups
-// (256 inputs for g = 8, 512 for g = 16). Within a super-chunk, lane quarter q
-// owns groups 8q .. 8q+7 -- one 16-byte load of codes per row tile -- and in
-// MFMA step s it feeds k-block g q + s of the super-chunk, in A and in B
-// alike, so the sum is unchanged. The four wavefronts take every fourth
+// Tiles. A workgroup of four wavefronts owns RT (2, 3 or 4) tiles of 16
+// output rows and all BP activation rows (NT tiles of 16): each decoded A
+// operand feeds NT MFMAs and each B operand RT MFMAs. K is walked in
+// super-chunks of 32 groups (256 inputs for g = 8, 512 for g = 16). Within a
+// super-chunk, lane quarter q owns groups 8q .. 8q+7 -- one 16-byte load of
+// codes per row tile -- and in MFMA step s it feeds k-block g q + s of the
+// super-chunk, in A and in B alike, so the sum is unchanged. The four wavefronts take every fourth
 // super-chunk of the workgroup's K range and add their float32 partial tiles
 // in LDS in wavefront order at the end.
 //
@@ -364,7 +364,9 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
 // clock model of one workgroup step round (four wavefronts, one MFMA step
 // each) -- MFMA issue, L1 accesses (one per 64-byte run a lane quad touches),
 // LDS codebook reads (2x8) or L2 codeword gathers (1x16) -- times the steps
-// per wavefront, times the rounds of workgroups over the CUs.
+// per wavefront, times the rounds of workgroups over the CUs. Three row
+// tiles exist for layers such as 11008 outputs, where four leave a third of
+// the CUs idle and two need a second round.
 struct MidPlan {
   int nt = 0, ntb = 0, rt = 0, splits = 0, nrb = 0;
   size_t xb_bytes = 0, part_off = 0, total = 0;
@@ -406,7 +408,7 @@ bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
   if ((L.out + 64) * row_bytes >= (int64_t(1) << 31) || xb_bytes + 4 * 65536 >= (int64_t(1) << 31))
     return false;
   double best = 0;
-  for (int rt : {4, 2}) {
+  for (int rt : {4, 3, 2}) {
     if (rt * nt > kMidMaxTiles) continue;
     const int64_t nrb = (L.out + 16 * rt - 1) / (16 * rt);
     const double mfma = 16.0 * rt * nt;
@@ -485,8 +487,11 @@ hipError_t launch_mid_t(const LayerDesc &L, const MidPlan &P, const uint16_t *x,
 template <Scheme S, int NT>
 hipError_t launch_mid_nt(const LayerDesc &L, const MidPlan &P, const uint16_t *x, int64_t batch,
                          uint16_t *y, uint8_t *ws, hipStream_t stream) {
-  return P.rt == 4 ? launch_mid_t<S, 4, NT>(L, P, x, batch, y, ws, stream)
-                   : launch_mid_t<S, 2, NT>(L, P, x, batch, y, ws, stream);
+  switch (P.rt) {
+    case 4: return launch_mid_t<S, 4, NT>(L, P, x, batch, y, ws, stream);
+    case 3: return launch_mid_t<S, 3, NT>(L, P, x, batch, y, ws, stream);
+    default: return launch_mid_t<S, 2, NT>(L, P, x, batch, y, ws, stream);
+  }
 }
 
 template <Scheme S>

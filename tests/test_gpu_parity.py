@@ -189,9 +189,10 @@ def test_workload_gemv(wname, lname, batch):
 
 
 # the workload's batches plus batches of the workspace GEMM (33..128 rows:
-# four row tiles per workgroup at 33/64 on the 11008-row layers, a half
-# chunk at the end of the 11008-input rows; 200 rows: two blocks of 128
-# activation rows on the layers whose wide grid would be small)
+# three row tiles per workgroup on the 11008-row layers, whose last row block
+# is a third full, a half chunk at the end of the 11008-input rows; 200 rows:
+# two blocks of 128 activation rows on the layers whose wide grid would be
+# small)
 GEMM_IDS = [(l.name, b) for l in WL.WORKLOADS["gemm_mlp"].layers
             for b in sorted(set(WL.WORKLOADS["gemm_mlp"].batches) | {33, 64, 100, 200})]
 
@@ -210,11 +211,13 @@ def test_workload_gemm(lname, batch):
 
 
 @pytest.mark.parametrize("sname", list(SCHEMES))
-@pytest.mark.parametrize("out,n_in,batch", [(100, 16384, 40), (40, 32768, 128), (1000, 8192, 20)])
+@pytest.mark.parametrize("out,n_in,batch", [(100, 16384, 40), (40, 32768, 128), (1000, 8192, 20),
+                                            (1035, 16384, 70)])
 def test_gemm_split_k(sname, out, n_in, batch):
     """Few output rows over a long K: the workspace form splits K across
-    workgroups and the last one to finish a row block adds the parts. Two calls
-    in a row (the arrival counters are re-zeroed per call) give the same bits."""
+    workgroups, which write float32 partial tiles that a second launch adds in
+    part order. 1035 rows take three row tiles per workgroup with a ragged last
+    block. Two calls in a row give the same bits."""
     s = SCHEMES[sname]
     codes, books, scales, x = WL.small_case(out, n_in, s, batch, seed=out + batch)
     layer = dev_layer(codes, books, scales)
