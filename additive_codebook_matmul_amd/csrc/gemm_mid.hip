@@ -213,6 +213,11 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
 #pragma unroll
     for (int j = 0; j < NT; ++j) bx[j] = buf_load16(xrs, base + (uint32_t)j * 256u);
   };
+  auto load_x1 = [&](int sc, int s, int j) __attribute__((always_inline)) {
+    const uint32_t base =
+        sc < sc_end ? x_lane + (uint32_t)sc * kScXBytes + (uint32_t)s * kBlockBytes : kMidOOB;
+    return buf_load16(xrs, base + (uint32_t)j * 256u);
+  };
   // 1x16: this lane's codeword (half, for g = 16) of step s
   auto gather = [&](const uint4 (&cw)[RT], int s, uint4 (&ga)[RT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -289,22 +294,38 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
         else
           decode(cw[K ^ 1], 0, a[(s + 1) & 1]);
       }
+      // the slot is refilled with step s + D (in the wave's next super-chunk
+      // past the end of this one)
+      const int sn = s + D < STEPS ? s + D : s + D - STEPS;
+      const int scn = s + D < STEPS ? sc : sc + kMidWaves;
+      if constexpr (LUT) {
+        // activation tile by activation tile: its RT MFMAs, then the refill
+        // of its B register, pinned in that order (left to itself the
+        // scheduler sinks the refills next to their use a step later, and
+        // every step then waits out the L2 latency)
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const uint4 at = LUT ? a[s & 1][t] : ga[LUT ? 0 : slot][t];
+        for (int j = 0; j < NT; ++j) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, at),
-                                                            __builtin_bit_cast(half8_t, bx[slot][j]),
-                                                            acc[t][j], 0, 0, 0);
-      }
-      // refill the slot with step s + D (in the wave's next super-chunk past the end of this one)
-      if (s + D < STEPS) {
-        load_x(sc, s + D, bx[slot]);
-        if constexpr (!LUT) gather(cw[K], s + D, ga[slot]);
+          for (int t = 0; t < RT; ++t)
+            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(half8_t, a[s & 1][t]), __builtin_bit_cast(half8_t, bx[slot][j]),
+                acc[t][j], 0, 0, 0);
+          bx[slot][j] = load_x1(scn, sn, j);
+          __builtin_amdgcn_sched_group_barrier(0x008, RT, 0);  // RT MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // then one vector-memory read
+        }
       } else {
-        load_x(sc + kMidWaves, s + D - STEPS, bx[slot]);
-        if constexpr (!LUT) gather(cw[K ^ 1], s + D - STEPS, ga[slot]);
+        // 1x16: each gathered A operand feeds its NT MFMAs in a row (the
+        // tile-by-tile order with pinned refills measured slower here)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(half8_t, ga[slot][t]), __builtin_bit_cast(half8_t, bx[slot][j]),
+                acc[t][j], 0, 0, 0);
+        load_x(scn, sn, bx[slot]);
+        gather(cw[s + D < STEPS ? K : K ^ 1], sn, ga[slot]);
       }
     }
     load_codes(sc + 2 * kMidWaves, cw[K]);
