@@ -218,6 +218,10 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
         sc < sc_end ? x_lane + (uint32_t)sc * kScXBytes + (uint32_t)s * kBlockBytes : kMidOOB;
     return buf_load16(xrs, base + (uint32_t)j * 256u);
   };
+  auto gather1 = [&](const uint4 &c, int s) __attribute__((always_inline)) {
+    const uint32_t code = code_of<G>(c, s);
+    return gbooks[G == 8 ? code : 2u * code + (uint32_t)(s & 1)];
+  };
   // 1x16: this lane's codeword (half, for g = 16) of step s
   auto gather = [&](const uint4 (&cw)[RT], int s, uint4 (&ga)[RT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -316,16 +320,28 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
         }
       } else {
         // 1x16: each gathered A operand feeds its NT MFMAs in a row (the
-        // tile-by-tile order with pinned refills measured slower here)
+        // tile-by-tile order measured slower here). Up to 64 activation rows
+        // each row tile's next codeword gather is pinned right after its
+        // MFMAs and the activation refills after the last tile; with more
+        // rows the L2 gather rate bounds the loop and pinning gains nothing.
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t) {
 #pragma unroll
           for (int j = 0; j < NT; ++j)
             acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 __builtin_bit_cast(half8_t, ga[slot][t]), __builtin_bit_cast(half8_t, bx[slot][j]),
                 acc[t][j], 0, 0, 0);
+          if constexpr (NT <= 4) {
+            ga[slot][t] = gather1(cw[s + D < STEPS ? K : K ^ 1][t], sn);
+            __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);  // NT MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // then the gather
+          }
+        }
         load_x(scn, sn, bx[slot]);
-        gather(cw[s + D < STEPS ? K : K ^ 1], sn, ga[slot]);
+        if constexpr (NT <= 4)
+          __builtin_amdgcn_sched_group_barrier(0x020, NT, 0);  // then the activations
+        else
+          gather(cw[s + D < STEPS ? K : K ^ 1], sn, ga[slot]);
       }
     }
     load_codes(sc + 2 * kMidWaves, cw[K]);
