@@ -37,6 +37,11 @@ hipError_t launch_gemv(const LayerDesc &L, const uint16_t *x, int batch, uint16_
                        hipStream_t stream);
 hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                        hipStream_t stream);
+// GEMV calls that the skinny matrix-core GEMM tiles (gemm.hip) serve faster
+// than the GEMV kernels, and their launch.
+bool gemv_uses_gemm_tiles(const LayerDesc &L, int batch);
+hipError_t launch_gemv_as_gemm(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
+                               hipStream_t stream);
 // Batched product with a caller-owned workspace (gemm_mid.hip): bytes the
 // workspace needs for this layer and batch (0: none, the call then runs
 // launch_gemm), and the launch itself.

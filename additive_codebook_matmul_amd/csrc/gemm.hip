@@ -619,4 +619,31 @@ hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uin
   return hipErrorInvalidValue;
 }
 
+// Token-generation calls (1..8 activation rows) that one 16-row skinny tile
+// serves faster than the GEMV kernels, measured per scheme on 4096 x 4096,
+// 11008 x 4096 and 4096 x 11008 layers: a 1x16 GEMV reads the activations
+// once per output row, so its cost grows with batch x in, and the 1x16 g16
+// GEMV (two 16-byte gathers per group and lane) already loses at two rows;
+// 2x8 only when its matrix-core GEMV cannot stage the activations in LDS
+// (the lookup kernel then costs 3x the tile at 5..8 rows of 11008 inputs).
+bool gemv_uses_gemm_tiles(const LayerDesc &L, int batch) {
+  if (batch < 2 || batch > 8 || !skinny_fits(L, batch, 1)) return false;
+  switch (L.scheme) {
+    case Scheme::k2x8: return batch >= 3 && !gemv_2x8_mfma_fits(L, batch);
+    case Scheme::k1x16: return (int64_t)batch * L.in >= 32768;
+    case Scheme::k1x16g16: return true;
+    default: return false;
+  }
+}
+
+hipError_t launch_gemv_as_gemm(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
+                               hipStream_t stream) {
+  switch (L.scheme) {
+    case Scheme::k2x8: return launch_skinny<Scheme::k2x8, 1>(L, x, batch, y, stream);
+    case Scheme::k1x16: return launch_skinny<Scheme::k1x16, 1>(L, x, batch, y, stream);
+    case Scheme::k1x16g16: return launch_skinny<Scheme::k1x16g16, 1>(L, x, batch, y, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace aqlm

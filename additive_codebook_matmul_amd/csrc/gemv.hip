@@ -538,6 +538,7 @@ hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int batch, uint1
 hipError_t launch_gemv(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
                        hipStream_t stream) {
   if (gemv_2x8_mfma_fits(L, batch)) return launch_gemv_2x8_mfma(L, x, batch, y, stream);
+  if (gemv_uses_gemm_tiles(L, batch)) return launch_gemv_as_gemm(L, x, batch, y, stream);
   switch (L.scheme) {
     case Scheme::k2x8: return launch_scheme<Scheme::k2x8>(L, x, batch, y, stream);
     case Scheme::k1x16: return launch_scheme<Scheme::k1x16>(L, x, batch, y, stream);

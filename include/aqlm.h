@@ -119,6 +119,9 @@ AQLM_API int aqlm_dequant(const aqlm_layer *layer, uint16_t *W, void *stream);
  * of "AQLM (additive / multi-codebook quantization)", field "Kernels").
  * x is [batch][in] float16, y is [batch][out] float16 (round to nearest
  * from a float32 accumulation). batch == 0 is a no-op returning AQLM_OK.
+ * Where a 16-row matrix-core tile of aqlm_gemm is faster for the batch
+ * (1x16 codes at several rows, 2x8 rows too long to stage 3..8 activation
+ * rows on chip) the call runs that tile; W is still never written.
  */
 AQLM_API int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
               uint16_t *y, void *stream);

@@ -53,6 +53,25 @@ def test_batched_shared_x_and_mixed_schemes():
         assert np.array_equal(bits(y), bits(L.gemv(dev_x(x))))
 
 
+@pytest.mark.parametrize("batch", [3, 5, 8])
+def test_batched_mixed_routes_bit_identical(batch):
+    """Layers that take the four GEMV routes (the matrix-core 2x8 GEMV, 2x8 rows
+    too long for it on the GEMM tiles from three rows, 1x16 g16 on the GEMM
+    tiles, short 1x16 rows on the lookup GEMV) in one grouped call: every
+    output equals its single-layer aqlm_gemv bit for bit and the oracle."""
+    specs = [(256, 4096, WL.S2x8), (200, 11008, WL.S2x8), (160, 2048, WL.S1x16g16),
+             (96, 1024, WL.S1x16)]
+    items = []
+    for i, (out, n_in, s) in enumerate(specs):
+        codes, books, scales, x = WL.small_case(out, n_in, s, batch, seed=70 + i)
+        items.append((codes, books, scales, x, dev_layer(codes, books, scales)))
+    ys = gemv_batched([it[4] for it in items], [dev_x(it[3]) for it in items])
+    for (codes, books, scales, x, L), y in zip(items, ys):
+        assert np.array_equal(bits(y), bits(L.gemv(dev_x(x)))), L.out_features
+        y_ref, bound = oracle.forward(x, codes, books, scales)
+        assert_product(y, y_ref, bound, f"batched mixed routes b{batch}")
+
+
 def test_batched_many_layers_splits_launches():
     """More layers than one grouped launch holds."""
     items = []

@@ -236,6 +236,27 @@ def test_gemm_split_k(sname, out, n_in, batch):
     assert np.array_equal(ys[0], ys[1])
 
 
+# GEMV calls that run on the 16-row GEMM tiles (2x8 rows too long to stage 5..8
+# activation rows on chip, 1x16 once batch x in reaches 32768, 1x16 g16 from
+# two rows) give exactly the bits of aqlm_gemm at that batch; the neighbours
+# on the GEMV side of each threshold are checked against the oracle too.
+@pytest.mark.parametrize("sname,out,n_in,batch,tiles", [
+    ("2x8", 4096, 11008, 4, False), ("2x8", 4096, 11008, 5, True), ("2x8", 4096, 11008, 8, True),
+    ("1x16", 1000, 11008, 2, False), ("1x16", 1000, 11008, 3, True),
+    ("1x16", 1000, 4096, 7, False), ("1x16", 1000, 4096, 8, True),
+    ("1x16g16", 300, 4096, 1, False), ("1x16g16", 300, 4096, 2, True)])
+def test_gemv_on_gemm_tiles(sname, out, n_in, batch, tiles):
+    s = SCHEMES[sname]
+    codes, books, scales, x = WL.small_case(out, n_in, s, batch, seed=out + n_in + batch)
+    layer = dev_layer(codes, books, scales)
+    y = layer.gemv(dev_x(x))
+    rows = _sample_rows(out, n=256)
+    y_ref, bound = oracle.forward_rows(x, codes, books, scales, rows)
+    assert_product(y.cpu().numpy()[:, rows], y_ref, bound, f"gemv {sname} {out}x{n_in} b{batch}")
+    if tiles:
+        assert np.array_equal(bits(y), bits(layer.gemm(dev_x(x), workspace=False)))
+
+
 # ---------------------------------------------------------------------------
 # probes the loose tolerance cannot replace
 # ---------------------------------------------------------------------------
