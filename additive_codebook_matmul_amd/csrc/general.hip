@@ -483,14 +483,14 @@ hipError_t launch_dequant_general(const LayerDesc &L, uint16_t *W, hipStream_t s
 
 hipError_t launch_gemv_general(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
                                hipStream_t stream) {
-  // 6..8 activation rows with at most three codebooks in element layout: the
-  // skinny GEMM's 16-row tile, which gathers each group's codewords once for
-  // all rows, beats the GEMV, whose cost grows by ~1.3 us per row on a
-  // 4096 x 4096 layer (measured on 1x8, 3x8 and 1x12 g8, 2x12 g16 and 2x16
-  // g8: 8 rows 21-29% faster). With four or more codebooks, or bit-packed
-  // codes, the tile's exact per-lane decode costs more and the GEMV stays
-  // ahead up to 8 rows.
-  if (batch >= 6 && L.M <= 3 && !L.packed && L.in * batch * 2 < ((int64_t)1 << 31))
+  // 6..8 activation rows with at most three codebooks in element layout (one
+  // with bit-packed codes): the skinny GEMM's 16-row tile, which gathers each
+  // group's codewords once for all rows, beats the GEMV, whose cost grows by
+  // ~1.3 us per row on a 4096 x 4096 layer (measured on 1x8, 3x8 and 1x12
+  // g8, 2x12 g16 and 2x16 g8: 8 rows 21-29% faster; packed 1x12 g8 20%).
+  // With more codebooks the tile's exact per-lane decode costs more and the
+  // GEMV stays ahead up to 8 rows.
+  if (batch >= 6 && L.M <= (L.packed ? 1 : 3) && L.in * batch * 2 < ((int64_t)1 << 31))
     return launch_gemm_general(L, x, batch, y, stream);
   const int cb = code_bytes(L);
   if (L.g == 8)

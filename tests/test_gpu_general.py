@@ -99,9 +99,12 @@ def test_packed_small(scheme, out, J):
     unpacked = oracle.unpack_codes(words, out, J, scheme.M, scheme.B)
     w_ref = oracle.decode(unpacked, books, scales)
     assert_bit_exact(layer.dequant().cpu().numpy(), w_ref, f"packed dequant {scheme.name} {out}x{J}")
-    for batch in (1, 5):
+    for batch in (1, 5, 6, 8):
         y_ref, bound = oracle.product(x[:batch], w_ref)
-        assert_product(layer.gemv(dev_x(x[:batch])), y_ref, bound, f"packed gemv {scheme.name} b{batch}")
+        y = layer.gemv(dev_x(x[:batch]))
+        assert_product(y, y_ref, bound, f"packed gemv {scheme.name} b{batch}")
+        if batch >= 6 and scheme.M == 1:  # served by the skinny GEMM tile
+            assert np.array_equal(bits(y), bits(layer.gemm(dev_x(x[:batch])))), batch
     for batch in (16, 70):
         y_ref, bound = oracle.product(x[:batch], w_ref)
         assert_product(layer.gemm(dev_x(x[:batch])), y_ref, bound, f"packed gemm {scheme.name} b{batch}")
