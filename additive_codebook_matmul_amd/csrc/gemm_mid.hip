@@ -157,6 +157,11 @@ __global__ __launch_bounds__(256) void gemm_mid_reduce_kernel(const float4_t *__
   store_out<NT>(y + (int64_t)tok0 * out, scales, out, batch - tok0, rb * 16 * RT, e, v);
 }
 
+// A lane's codes of one super-chunk under 1x16 g16: 16 groups, two loads.
+struct CodePair {
+  uint4 lo, hi;
+};
+
 template <Scheme S, int RT, int NT>
 __global__ __launch_bounds__(kMidThreads)
 __attribute__((amdgpu_waves_per_eu(kMidOccupancy, kMidOccupancy)))
@@ -167,6 +172,11 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   using C = MidCfg<S>;
   constexpr int G = C::G, STEPS = C::STEPS;
   constexpr bool LUT = S == Scheme::k2x8;
+  // 1x16 g16: lane quarters 2p and 2p + 1 take the two 16-byte halves of the
+  // same codeword in every step (pair p walks groups 16p .. 16p + 15 of the
+  // super-chunk, one per step), so one gather instruction fetches both halves
+  constexpr bool PAIR = S == Scheme::k1x16g16;
+  using CW = std::conditional_t<PAIR, CodePair, uint4>;
   constexpr int BP = 16 * NT;      // activation rows of a workgroup (one slab of xb)
   constexpr int E = RT * NT * 64;  // float4 accumulators of a workgroup tile
   constexpr int D = ring_depth(RT, NT);
@@ -198,36 +208,69 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   const uint32_t x_lane = ((uint32_t)(q * G * BP) + (uint32_t)r) * 16u;
   constexpr uint32_t kBlockBytes = BP * 16u;  // one k-block of the slab
   constexpr uint32_t kScXBytes = C::SC_BLOCKS * kBlockBytes;
+  // paired form: pair p = q / 2 reads codes 32 p .. 32 p + 31 of the
+  // super-chunk's 64 code bytes; in step s lane quarter q feeds k-block
+  // 2 (16 p + s) + q % 2, in A and in B alike
+  const int pq = q >> 1, hq = q & 1;
+  const uint32_t code_pair = (uint32_t)(row0 + r) * row_bytes + (uint32_t)pq * 32u;
+  const uint32_t x_pair = ((uint32_t)((32 * pq + hq) * BP) + (uint32_t)r) * 16u;
 
-  // this lane's 16 code bytes of super-chunk sc for every row tile
-  auto load_codes = [&](int sc, uint4 (&cw)[RT]) __attribute__((always_inline)) {
-    const bool ok = sc < sc_end && sc * kGroupsPerSc + 8 * q < groups;
-    const uint32_t base = ok ? code_lane + (uint32_t)sc * (kGroupsPerSc * 2u) : kMidOOB;
+  // this lane's code bytes of super-chunk sc for every row tile
+  auto load_codes = [&](int sc, CW (&cw)[RT]) __attribute__((always_inline)) {
+    if constexpr (PAIR) {
+      const int g0 = sc * kGroupsPerSc + 16 * pq;
+      const uint32_t b = code_pair + (uint32_t)sc * (kGroupsPerSc * 2u);
+      const uint32_t blo = sc < sc_end && g0 < groups ? b : kMidOOB;
+      const uint32_t bhi = sc < sc_end && g0 + 8 < groups ? b + 16u : kMidOOB;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) cw[t] = buf_load16(crs, base + (uint32_t)t * 16u * row_bytes);
+      for (int t = 0; t < RT; ++t) {
+        cw[t].lo = buf_load16(crs, blo + (uint32_t)t * 16u * row_bytes);
+        cw[t].hi = buf_load16(crs, bhi + (uint32_t)t * 16u * row_bytes);
+      }
+    } else {
+      const bool ok = sc < sc_end && sc * kGroupsPerSc + 8 * q < groups;
+      const uint32_t base = ok ? code_lane + (uint32_t)sc * (kGroupsPerSc * 2u) : kMidOOB;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) cw[t] = buf_load16(crs, base + (uint32_t)t * 16u * row_bytes);
+    }
   };
-  // B operands of step s of super-chunk sc (k-block g q + s, rows 16 j + r)
+  // B operands of step s of super-chunk sc (k-block g q + s, or the paired
+  // form's, rows 16 j + r)
+  auto x_at = [&](int sc, int s) __attribute__((always_inline)) {
+    if constexpr (PAIR)
+      return sc < sc_end ? x_pair + (uint32_t)sc * kScXBytes + (uint32_t)s * 2u * kBlockBytes
+                         : kMidOOB;
+    else
+      return sc < sc_end ? x_lane + (uint32_t)sc * kScXBytes + (uint32_t)s * kBlockBytes : kMidOOB;
+  };
   auto load_x = [&](int sc, int s, uint4 (&bx)[NT]) __attribute__((always_inline)) {
-    const uint32_t base =
-        sc < sc_end ? x_lane + (uint32_t)sc * kScXBytes + (uint32_t)s * kBlockBytes : kMidOOB;
+    const uint32_t base = x_at(sc, s);
 #pragma unroll
     for (int j = 0; j < NT; ++j) bx[j] = buf_load16(xrs, base + (uint32_t)j * 256u);
   };
   auto load_x1 = [&](int sc, int s, int j) __attribute__((always_inline)) {
-    const uint32_t base =
-        sc < sc_end ? x_lane + (uint32_t)sc * kScXBytes + (uint32_t)s * kBlockBytes : kMidOOB;
-    return buf_load16(xrs, base + (uint32_t)j * 256u);
-  };
-  auto gather1 = [&](const uint4 &c, int s) __attribute__((always_inline)) {
-    const uint32_t code = code_of<G>(c, s);
-    return gbooks[G == 8 ? code : 2u * code + (uint32_t)(s & 1)];
+    return buf_load16(xrs, x_at(sc, s) + (uint32_t)j * 256u);
   };
   // 1x16: this lane's codeword (half, for g = 16) of step s
-  auto gather = [&](const uint4 (&cw)[RT], int s, uint4 (&ga)[RT]) __attribute__((always_inline)) {
+  auto gather1 = [&](const CW &c, int s) __attribute__((always_inline)) {
+    if constexpr (PAIR) {
+      const uint32_t code = code_of<8>(s < 8 ? c.lo : c.hi, s & 7);
+      return gbooks[2u * code + (uint32_t)hq];
+    } else {
+      const uint32_t code = code_of<G>(c, s);
+      return gbooks[G == 8 ? code : 2u * code + (uint32_t)(s & 1)];
+    }
+  };
+  auto gather = [&](const CW (&cw)[RT], int s, uint4 (&ga)[RT]) __attribute__((always_inline)) {
+    if constexpr (PAIR) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const uint32_t code = code_of<G>(cw[t], s);
-      ga[t] = gbooks[G == 8 ? code : 2u * code + (uint32_t)(s & 1)];
+      for (int t = 0; t < RT; ++t) ga[t] = gather1(cw[t], s);
+    } else {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint32_t code = code_of<G>(cw[t], s);
+        ga[t] = gbooks[G == 8 ? code : 2u * code + (uint32_t)(s & 1)];
+      }
     }
   };
   // 2x8: the fp16 sum of the two codewords of step s. A table address is
@@ -237,7 +280,7 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   const uint32_t mA = (uint32_t)(r >> 3), mB = mA ^ 1u;
   const uint32_t selA[2] = {0x0C0C0000u | ((4u + mA) << 8), 0x0C0C0000u | ((6u + mA) << 8)};
   const uint32_t selB[2] = {0x0C0C0000u | ((4u + mB) << 8), 0x0C0C0000u | ((6u + mB) << 8)};
-  auto decode = [&](const uint4 (&cw)[RT], int s, uint4 (&a)[RT]) __attribute__((always_inline)) {
+  auto decode = [&](const auto &cw, int s, uint4 (&a)[RT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const uint32_t word = (s >> 1) == 0 ? cw[t].x : (s >> 1) == 1 ? cw[t].y
@@ -256,7 +299,7 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
     for (int j = 0; j < NT; ++j) acc[t][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   int sc = (int)((int64_t)sp * nsc / splits) + w;
-  uint4 cw[2][RT];  // codes of this and of the wave's next super-chunk (static ring)
+  CW cw[2][RT];  // codes of this and of the wave's next super-chunk (static ring)
   uint4 bx[D][NT];
   uint4 ga[LUT ? 1 : D][RT];
   uint4 a[2][RT];
