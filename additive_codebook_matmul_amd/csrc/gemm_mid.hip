@@ -471,8 +471,8 @@ bool mid_beats_wide(const LayerDesc &L, int64_t batch) {
 }
 
 bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
-  if (L.scheme == Scheme::kGeneral || L.packed || batch < kMidMinBatch || batch > kMidMaxBatch)
-    return false;
+  // (bit-packed 8- and 16-bit codes are the element layout's bytes)
+  if (L.scheme == Scheme::kGeneral || batch < kMidMinBatch || batch > kMidMaxBatch) return false;
   if (L.groups % 8 != 0) return false;  // a lane's 16 code bytes never straddle a row end
   const int G = group_size(L.scheme);
   const int steps = G;

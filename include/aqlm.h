@@ -149,7 +149,7 @@ AQLM_API int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, in
 /*
  * aqlm_gemm_ws: the product of aqlm_gemm with a caller-owned device
  * workspace, which lets the three dedicated schemes (2x8, 1x16 and 1x16 with
- * g = 16; element codes, in / g a multiple of 8) run the workspace form of
+ * g = 16; element or bit-packed codes, in / g a multiple of 8) run the workspace form of
  * the matrix-core path from 17 activation rows up to the batch where the
  * wide tiles of aqlm_gemm fill the chip by themselves (at most 4096 rows):
  * the activations are first re-laid into blocks of 8 inputs so that every

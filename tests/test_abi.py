@@ -129,9 +129,9 @@ def _ws_size(s, batch):
 
 def test_workspace_size():
     """Host-side sizing: the workspace form covers 17 rows and up (while the
-    wide tiles' grid is small) of the three
-    dedicated schemes with element codes and in/g a multiple of 8; it holds at
-    least the re-laid activations (in x 16*ceil(batch/16) float16 values)."""
+    wide tiles' grid is small) of the three dedicated schemes (element or
+    bit-packed codes) with in/g a multiple of 8; it holds at least the re-laid
+    activations (in x 16*ceil(batch/16) float16 values)."""
     mlp = dict(out=4096, n_in=11008)
     for M, B, g in ((2, 8, 8), (1, 16, 8), (1, 16, 16)):
         for batch in (17, 33, 64, 100, 128):
@@ -145,7 +145,8 @@ def test_workspace_size():
     assert _ws_size(_layer(**mlp), 4096) == (0, 0)                   # the wide tiles fill the chip
     assert _ws_size(_layer(out=11008, n_in=4096), 1024) == (0, 0)
     assert _ws_size(_layer(3, 8, 8, **mlp), 64) == (0, 0)            # general scheme
-    assert _ws_size(_layer(flags=1, **mlp), 64) == (0, 0)            # bit-packed codes
+    assert _ws_size(_layer(flags=1, **mlp), 64) == _ws_size(_layer(**mlp), 64)  # same bytes
+    assert _ws_size(_layer(3, 8, 8, flags=1, **mlp), 64) == (0, 0)   # general, bit-packed
     assert _ws_size(_layer(out=64, n_in=36 * 8), 64) == (0, 0)       # in/g not a multiple of 8
     assert _ws_size(_layer(codes=0, **mlp), 64) == (1, 0)
     assert _ws_size(_layer(**mlp), -1) == (5, 0)

@@ -257,6 +257,32 @@ def test_gemv_on_gemm_tiles(sname, out, n_in, batch, tiles):
         assert np.array_equal(bits(y), bits(layer.gemm(dev_x(x), workspace=False)))
 
 
+@pytest.mark.parametrize("sname", list(SCHEMES))
+def test_dedicated_schemes_bit_packed(sname):
+    """The bit-packed flag on a dedicated scheme (8- or 16-bit codes, where the
+    stream holds the element layout's bytes) gives the element layout's bits
+    on every entry point and route."""
+    s = SCHEMES[sname]
+    out, n_in = 300, 64 * s.g
+    codes, books, scales, x = WL.small_case(out, n_in, s, 130, seed=21)
+    plain = dev_layer(codes, books, scales)
+    words = WL.pack_codes(codes, s.B)
+    packed = AqlmLayer(torch.from_numpy(words.view(np.int32)).to(device()),
+                       torch.from_numpy(books).to(device()), torch.from_numpy(scales).to(device()),
+                       in_features=n_in)
+    assert np.array_equal(bits(packed.dequant()), bits(plain.dequant()))
+    for batch in (1, 2, 5, 8):
+        xb = dev_x(x[:batch])
+        assert np.array_equal(bits(packed.gemv(xb)), bits(plain.gemv(xb))), batch
+    for batch in (16, 64, 130):
+        xb = dev_x(x[:batch])
+        for ws in (True, False):
+            assert np.array_equal(bits(packed.gemm(xb, workspace=ws)),
+                                  bits(plain.gemm(xb, workspace=ws))), (batch, ws)
+    y_ref, bound = oracle.forward(x[:8], codes, books, scales)
+    assert_product(packed.gemv(dev_x(x[:8])), y_ref, bound, f"packed {sname} gemv b8")
+
+
 # ---------------------------------------------------------------------------
 # probes the loose tolerance cannot replace
 # ---------------------------------------------------------------------------
