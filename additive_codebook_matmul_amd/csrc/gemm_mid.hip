@@ -11,8 +11,9 @@
 // inputs, one slab per block of BP = 16 NT activation rows,
 //   xb[tb][kb][t][0..7] = x[tb BP + t][8 kb .. 8 kb + 7]    (zero past batch),
 // after which the B operand of one MFMA step for 16 activation rows is one
-// contiguous 256-byte run, and the k-block stride is a compile-time constant. The workspace also holds the float32 partial tiles
-// of the split-K form below.
+// contiguous 256-byte run, and the k-block stride is a compile-time constant.
+// The workspace also holds the float32 partial tiles of the split-K form
+// below.
 //
 // Tiles. A workgroup of four wavefronts owns RT (2, 3 or 4) tiles of 16
 // output rows and all BP activation rows (NT tiles of 16): each decoded A
@@ -20,7 +21,9 @@
 // super-chunks of 32 groups (256 inputs for g = 8, 512 for g = 16). Within a
 // super-chunk, lane quarter q owns groups 8q .. 8q+7 -- one 16-byte load of
 // codes per row tile -- and in MFMA step s it feeds k-block g q + s of the
-// super-chunk, in A and in B alike, so the sum is unchanged. The four wavefronts take every fourth
+// super-chunk, in A and in B alike, so the sum is unchanged. (1x16 g16 pairs
+// the quarters instead: 2p and 2p + 1 take the two halves of group 16p + s
+// in step s; see PAIR below.) The four wavefronts take every fourth
 // super-chunk of the workgroup's K range and add their float32 partial tiles
 // in LDS in wavefront order at the end.
 //
