@@ -139,6 +139,52 @@ __global__ __launch_bounds__(kBlock) void gemm_wide_kernel(
     constexpr bool MASK = decltype(masked)::value;
     const uint16_t *xt = lds_x[buf];
     constexpr int STEPS = C::G == 8 ? 4 : 8;
+    if constexpr (S == Scheme::k2x8) {
+      // 2x8: the LDS reads of step s + 1 (two codeword pairs, NI activation
+      // fragments) are issued before the MFMAs of step s and the codeword
+      // sums taken after them, so LDS latency (bank conflicts included:
+      // random codes) overlaps the matrix cores instead of preceding them
+      uint4 c0[2][2], c1[2][2], bx[2][NI];
+      auto reads = [&](int s, int slot) __attribute__((always_inline)) {
+        const int kcol = (half * 4 + s) * 8;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const uint32_t code = (cw[mi][s >> 1] >> ((s & 1) * 16)) & 0xFFFFu;
+          c0[slot][mi] = lds_books[code & 0xFF];
+          c1[slot][mi] = lds_books[256 + (code >> 8)];
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          bx[slot][ni] =
+              *reinterpret_cast<const uint4 *>(&xt[(ni * 32 + l32) * C::ROW_HALVES + kcol]);
+      };
+      reads(0, 0);
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        const int cur = s & 1;
+        uint4 a[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          a[mi] = hadd8(c0[cur][mi], c1[cur][mi]);
+          if constexpr (MASK) {
+            if (kb * kKG + half * 4 + s >= groups) a[mi] = make_uint4(0, 0, 0, 0);
+          }
+        }
+        if (s + 1 < STEPS) reads(s + 1, cur ^ 1);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(half8_t, a[mi]), __builtin_bit_cast(half8_t, bx[cur][ni]),
+                acc[mi][ni], 0, 0, 0);
+        if (s + 1 < STEPS) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 + NI, 0);  // next step's LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NI, 0);  // then this step's MFMAs
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       // K columns of this step for this lane half, within the K block
