@@ -1,4 +1,4 @@
-// Batched product y = x . W^T for 17 and more activation rows with a caller-owned
+// Batched product y = x . W^T for any number of activation rows with a caller-owned
 // device workspace (aqlm_gemm_ws). The weights are decoded on chip straight
 // into the A operand of v_mfma_f32_16x16x32_f16 (float32 accumulation) and
 // are never written to memory.
@@ -63,7 +63,7 @@ constexpr int kMidWaves = 4;
 constexpr int kMidThreads = 64 * kMidWaves;
 constexpr int kGroupsPerSc = 32;  // groups per super-chunk
 constexpr uint32_t kMidOOB = 0x80000000u;
-constexpr int64_t kMidMinBatch = 17;  // up to 16 rows the skinny kernel of aqlm_gemm is as fast
+constexpr int64_t kMidMinBatch = 1;
 constexpr int64_t kMidMaxBatch = 4096;
 constexpr int kMidCus = 256;
 constexpr int kMidOccupancy = 1;  // wavefronts per SIMD the kernel is built for
@@ -517,6 +517,12 @@ bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
     }
   }
   if (p->nt == 0) return false;
+  // Up to 16 rows aqlm_gemm's skinny tile is as fast as this form once K has
+  // to be split (the reduce launch then costs what the tile saves) or when
+  // the row blocks leave most CUs idle anyway (the re-layout launch is then
+  // pure overhead); with neither, this form is 20-28% faster (11008 x 4096,
+  // 1..16 rows).
+  if (batch <= 16 && (p->splits > 1 || p->nrb * p->ntb < kMidCus / 2)) return false;
   p->xb_bytes = (size_t)xb_bytes;
   p->part_off = align256((size_t)xb_bytes);
   p->total = p->part_off +
@@ -581,6 +587,7 @@ template <Scheme S>
 hipError_t launch_mid_s(const LayerDesc &L, const MidPlan &P, const uint16_t *x, int64_t batch,
                         uint16_t *y, uint8_t *ws, hipStream_t stream) {
   switch (P.nt) {
+    case 1: return launch_mid_nt<S, 1>(L, P, x, batch, y, ws, stream);
     case 2: return launch_mid_nt<S, 2>(L, P, x, batch, y, ws, stream);
     case 3: return launch_mid_nt<S, 3>(L, P, x, batch, y, ws, stream);
     case 4: return launch_mid_nt<S, 4>(L, P, x, batch, y, ws, stream);

@@ -188,13 +188,15 @@ def test_workload_gemv(wname, lname, batch):
         assert_product(y, y_ref, bound, f"{wname}/{lname} b{batch}")
 
 
-# the workload's batches plus batches of the workspace GEMM (33..128 rows:
+# the workload's batches plus batches of the workspace GEMM (1..16 rows: one
+# activation tile on the 11008-row layers, the skinny tile on the others;
+# 33..128 rows:
 # three row tiles per workgroup on the 11008-row layers, whose last row block
 # is a third full, a half chunk at the end of the 11008-input rows; 200 rows:
 # two blocks of 128 activation rows on the layers whose wide grid would be
 # small)
 GEMM_IDS = [(l.name, b) for l in WL.WORKLOADS["gemm_mlp"].layers
-            for b in sorted(set(WL.WORKLOADS["gemm_mlp"].batches) | {33, 64, 100, 200})]
+            for b in sorted(set(WL.WORKLOADS["gemm_mlp"].batches) | {1, 8, 33, 64, 100, 200})]
 
 
 @pytest.mark.parametrize("lname,batch", GEMM_IDS, ids=lambda v: str(v))
