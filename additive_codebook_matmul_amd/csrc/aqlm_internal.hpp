@@ -46,6 +46,10 @@ hipError_t launch_gemv_as_gemm(const LayerDesc &L, const uint16_t *x, int batch,
 // workspace needs for this layer and batch (0: none, the call then runs
 // launch_gemm), and the launch itself.
 int64_t gemm_ws_bytes(const LayerDesc &L, int64_t batch);
+// The same form at one activation tile (1..16 rows) where it needs no
+// workspace at all (activations read in place, K not split); launch_gemm and
+// the GEMV route to it when true, through launch_gemm_ws with no workspace.
+bool gemm_mid_direct(const LayerDesc &L, int64_t batch);
 hipError_t launch_gemm_ws(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                           void *ws, hipStream_t stream);
 // Kernels for Scheme::kGeneral (general.hip).

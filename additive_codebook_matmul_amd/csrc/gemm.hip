@@ -643,6 +643,8 @@ hipError_t launch_wide(const LayerDesc &L, const uint16_t *x, int64_t batch, uin
 template <Scheme S>
 hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                          hipStream_t stream) {
+  // one activation tile of the workspace form, where it needs no workspace
+  if (gemm_mid_direct(L, batch)) return launch_gemm_ws(L, x, batch, y, nullptr, stream);
   if (batch <= 16 && skinny_fits(L, batch, 1)) return launch_skinny<S, 1>(L, x, batch, y, stream);
   if (batch <= kSkinnyMaxBatch && skinny_fits(L, batch, 2))
     return launch_skinny<S, 2>(L, x, batch, y, stream);
@@ -684,6 +686,7 @@ bool gemv_uses_gemm_tiles(const LayerDesc &L, int batch) {
 
 hipError_t launch_gemv_as_gemm(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
                                hipStream_t stream) {
+  if (gemm_mid_direct(L, batch)) return launch_gemm_ws(L, x, batch, y, nullptr, stream);
   switch (L.scheme) {
     case Scheme::k2x8: return launch_skinny<Scheme::k2x8, 1>(L, x, batch, y, stream);
     case Scheme::k1x16: return launch_skinny<Scheme::k1x16, 1>(L, x, batch, y, stream);

@@ -13,7 +13,10 @@
 // after which the B operand of one MFMA step for 16 activation rows is one
 // contiguous 256-byte run, and the k-block stride is a compile-time constant.
 // The workspace also holds the float32 partial tiles of the split-K form
-// below.
+// below. With one activation tile (NT = 1, up to 16 rows) there is no
+// re-layout: a lane's 16-byte pieces of its activation row stay in one
+// 128-byte line for the steps that use them, so the B operands are loaded
+// from x in place, and with K unsplit the form needs no workspace at all.
 //
 // Tiles. A workgroup of four wavefronts owns RT (2, 3 or 4) tiles of 16
 // output rows and all BP activation rows (NT tiles of 16): each decoded A
@@ -180,6 +183,11 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   // super-chunk, one per step), so one gather instruction fetches both halves
   constexpr bool PAIR = S == Scheme::k1x16g16;
   using CW = std::conditional_t<PAIR, CodePair, uint4>;
+  // one activation tile: B fragments straight from x [batch][in] (a lane's
+  // 16-byte pieces of one row stay in one 128-byte line for the 8 steps that
+  // use them, so the L1 serves all but the first); xb is then x itself and
+  // slab_bytes its size
+  constexpr bool DIRECT = NT == 1;
   constexpr int BP = 16 * NT;      // activation rows of a workgroup (one slab of xb)
   constexpr int E = RT * NT * 64;  // float4 accumulators of a workgroup tile
   constexpr int D = ring_depth(RT, NT);
@@ -201,7 +209,7 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   const int sc_end = (int)((int64_t)(sp + 1) * nsc / splits);
   const uint32_t row_bytes = (uint32_t)groups * 2u;
   const Rsrc crs = make_rsrc(codes, codes_bytes);
-  const Rsrc xrs = make_rsrc(xb + (size_t)blockIdx.y * (slab_bytes / 16u), slab_bytes);
+  const Rsrc xrs = make_rsrc(DIRECT ? xb : xb + (size_t)blockIdx.y * (slab_bytes / 16u), slab_bytes);
   const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
 
   // the row scales for the epilogue (read after the barriers that end the K loop)
@@ -239,8 +247,13 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   };
   // B operands of step s of super-chunk sc (k-block g q + s, or the paired
   // form's, rows 16 j + r)
+  const int nkb = groups * (G / 8);                       // k-blocks of a row
+  const uint32_t x_row = (uint32_t)r * (uint32_t)nkb * 16u;  // row r of x (past batch: out of range)
   auto x_at = [&](int sc, int s) __attribute__((always_inline)) {
-    if constexpr (PAIR)
+    if constexpr (DIRECT) {
+      const int kb = sc * C::SC_BLOCKS + (PAIR ? 32 * pq + hq + 2 * s : G * q + s);
+      return sc < sc_end && kb < nkb ? x_row + (uint32_t)kb * 16u : kMidOOB;
+    } else if constexpr (PAIR)
       return sc < sc_end ? x_pair + (uint32_t)sc * kScXBytes + (uint32_t)s * 2u * kBlockBytes
                          : kMidOOB;
     else
@@ -486,9 +499,10 @@ bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
   const int64_t bp = 16 * nt * ntb;
   const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
   const int64_t nsc = (L.groups + kGroupsPerSc - 1) / kGroupsPerSc;
-  const int64_t xb_bytes = L.in * bp * 2;
+  // one activation tile reads x directly: no re-laid copy
+  const int64_t xb_bytes = nt == 1 ? 0 : L.in * bp * 2;
   // 32-bit buffer offsets, with room for the out-of-range marker
-  if ((L.out + 64) * row_bytes >= (int64_t(1) << 31) || xb_bytes + 4 * 65536 >= (int64_t(1) << 31))
+  if ((L.out + 64) * row_bytes >= (int64_t(1) << 31) || L.in * bp * 2 + 4 * 65536 >= (int64_t(1) << 31))
     return false;
   double best = 0;
   for (int rt : {4, 3, 2}) {
@@ -551,20 +565,26 @@ hipError_t launch_mid_t(const LayerDesc &L, const MidPlan &P, const uint16_t *x,
       raised.fetch_or(bit, std::memory_order_acq_rel);
     }
   }
-  uint4 *xb = reinterpret_cast<uint4 *>(ws);
   float4_t *part = reinterpret_cast<float4_t *>(ws + P.part_off);
-  const int nkb = (int)(L.in / 8);
-  hipLaunchKernelGGL(gemm_xblock_kernel, dim3((unsigned)((nkb + 15) / 16), (unsigned)(NT * P.ntb)),
-                     dim3(256), 0, stream, reinterpret_cast<const uint4 *>(x), xb, nkb, (int)batch,
-                     16 * NT);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const uint4 *xb = reinterpret_cast<const uint4 *>(ws);
+  uint32_t slab = (uint32_t)(P.xb_bytes / P.ntb);
+  if constexpr (NT == 1) {
+    // one activation tile reads x in place
+    xb = reinterpret_cast<const uint4 *>(x);
+    slab = (uint32_t)(batch * L.in * 2);
+  } else {
+    const int nkb = (int)(L.in / 8);
+    hipLaunchKernelGGL(gemm_xblock_kernel, dim3((unsigned)((nkb + 15) / 16), (unsigned)(NT * P.ntb)),
+                       dim3(256), 0, stream, reinterpret_cast<const uint4 *>(x),
+                       reinterpret_cast<uint4 *>(ws), nkb, (int)batch, 16 * NT);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL(k, dim3((unsigned)(P.nrb * P.splits), (unsigned)P.ntb), dim3(kMidThreads), lds,
                      stream, static_cast<const uint8_t *>(L.codes), L.books, L.scales, xb, y, part,
                      (int)L.out, (int)L.groups, (int)batch, P.splits,
-                     (uint32_t)(L.out * L.groups * kCodeBytesPerGroup),
-                     (uint32_t)(P.xb_bytes / P.ntb));
-  e = hipGetLastError();
+                     (uint32_t)(L.out * L.groups * kCodeBytesPerGroup), slab);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.splits == 1) return e;
   constexpr int E = RT * NT * 64;
   hipLaunchKernelGGL((gemm_mid_reduce_kernel<RT, NT>),
@@ -597,6 +617,11 @@ hipError_t launch_mid_s(const LayerDesc &L, const MidPlan &P, const uint16_t *x,
 }
 
 }  // namespace
+
+bool gemm_mid_direct(const LayerDesc &L, int64_t batch) {
+  MidPlan p;
+  return batch <= 16 && mid_plan(L, batch, &p) && p.total == 0;
+}
 
 int64_t gemm_ws_bytes(const LayerDesc &L, int64_t batch) {
   MidPlan p;

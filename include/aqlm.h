@@ -150,10 +150,12 @@ AQLM_API int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, in
  * aqlm_gemm_ws: the product of aqlm_gemm with a caller-owned device
  * workspace, which lets the three dedicated schemes (2x8, 1x16 and 1x16 with
  * g = 16; element or bit-packed codes, in / g a multiple of 8) run the
- * workspace form of the matrix-core path up to the batch where the wide
- * tiles of aqlm_gemm fill the chip by themselves (at most 4096 rows; at
- * 1..16 rows only where its row blocks fill half the chip without splitting
- * K): the activations are first re-laid into blocks of 8 inputs so that every
+ * workspace form of the matrix-core path from 17 rows up to the batch where
+ * the wide tiles of aqlm_gemm fill the chip by themselves (at most 4096
+ * rows). (At 1..16 rows, on layers whose row blocks fill half the chip
+ * without splitting K, the same form reads x in place and needs no
+ * workspace; aqlm_gemm and aqlm_gemv run it there themselves.) From 17 rows
+ * the activations are first re-laid into blocks of 8 inputs so that every
  * MFMA operand load is contiguous, rows beyond 128 go to blocks of 128, and
  * K may be split across workgroups whose float32 partial sums meet in the
  * workspace. Every other case runs as aqlm_gemm and ignores the workspace.

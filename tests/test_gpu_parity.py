@@ -246,7 +246,9 @@ def test_gemm_split_k(sname, out, n_in, batch):
     ("2x8", 4096, 11008, 4, False), ("2x8", 4096, 11008, 5, True), ("2x8", 4096, 11008, 8, True),
     ("1x16", 1000, 11008, 2, False), ("1x16", 1000, 11008, 3, True),
     ("1x16", 1000, 4096, 7, False), ("1x16", 1000, 4096, 8, True),
-    ("1x16g16", 300, 4096, 1, False), ("1x16g16", 300, 4096, 2, True)])
+    ("1x16g16", 300, 4096, 1, False), ("1x16g16", 300, 4096, 2, True),
+    # layers whose GEMM tile is the workspace form's one activation tile read in place
+    ("1x16g16", 11008, 4096, 2, True), ("1x16", 11008, 4096, 8, True), ("2x8", 7000, 2112, 3, True)])
 def test_gemv_on_gemm_tiles(sname, out, n_in, batch, tiles):
     s = SCHEMES[sname]
     codes, books, scales, x = WL.small_case(out, n_in, s, batch, seed=out + n_in + batch)
@@ -257,6 +259,23 @@ def test_gemv_on_gemm_tiles(sname, out, n_in, batch, tiles):
     assert_product(y.cpu().numpy()[:, rows], y_ref, bound, f"gemv {sname} {out}x{n_in} b{batch}")
     if tiles:
         assert np.array_equal(bits(y), bits(layer.gemm(dev_x(x), workspace=False)))
+
+
+@pytest.mark.parametrize("batch", [1, 7, 16])
+def test_gemm_one_tile_in_place(batch):
+    """Up to 16 rows, on layers with enough row blocks, the product runs one
+    activation tile of the workspace form reading x in place: no workspace,
+    the same bits with and without one. 2112 inputs leave a quarter-full last
+    super-chunk; 7000 rows a ragged last row block."""
+    s = SCHEMES["2x8"]
+    codes, books, scales, x = WL.small_case(7000, 2112, s, batch, seed=batch)
+    layer = dev_layer(codes, books, scales)
+    assert layer.workspace_bytes(batch) == 0
+    y = layer.gemm(dev_x(x), workspace=False)
+    assert np.array_equal(bits(y), bits(layer.gemm(dev_x(x), workspace=True)))
+    rows = _sample_rows(7000, n=512)
+    y_ref, bound = oracle.forward_rows(x, codes, books, scales, rows)
+    assert_product(y.cpu().numpy()[:, rows], y_ref, bound, f"one tile in place b{batch}")
 
 
 @pytest.mark.parametrize("sname", list(SCHEMES))
