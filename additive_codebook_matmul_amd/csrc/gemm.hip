@@ -658,6 +658,11 @@ hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int64_t batch, u
 
 hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                        hipStream_t stream) {
+  // Up to 8 rows the token-generation routes (matrix-core or lookup GEMV, or a
+  // 16-row GEMM tile where that measured faster) are the fastest form of the
+  // same product for every scheme: the call runs them, bit-identical to
+  // aqlm_gemv.
+  if (batch <= 8) return launch_gemv(L, x, (int)batch, y, stream);
   switch (L.scheme) {
     case Scheme::k2x8: return launch_scheme<Scheme::k2x8>(L, x, batch, y, stream);
     case Scheme::k1x16: return launch_scheme<Scheme::k1x16>(L, x, batch, y, stream);
@@ -667,19 +672,24 @@ hipError_t launch_gemm(const LayerDesc &L, const uint16_t *x, int64_t batch, uin
   return hipErrorInvalidValue;
 }
 
-// Token-generation calls (1..8 activation rows) that one 16-row skinny tile
+// Token-generation calls (1..8 activation rows) that a 16-row GEMM tile
 // serves faster than the GEMV kernels, measured per scheme on 4096 x 4096,
-// 11008 x 4096 and 4096 x 11008 layers: a 1x16 GEMV reads the activations
-// once per output row, so its cost grows with batch x in, and the 1x16 g16
-// GEMV (two 16-byte gathers per group and lane) already loses at two rows;
-// 2x8 only when its matrix-core GEMV cannot stage the activations in LDS
-// (the lookup kernel then costs 3x the tile at 5..8 rows of 11008 inputs).
+// 11008 x 4096 and 4096 x 11008 layers. The tile is the workspace form's
+// one activation tile read in place where that applies (layers with enough
+// row blocks to fill half the chip unsplit), else the skinny tile. A 1x16
+// GEMV reads the activations once per output row, so its cost grows with
+// batch x in; the 1x16 g16 GEMV (two 16-byte gathers per group and lane)
+// loses from two rows, and from one row against the in-place tile; 2x8
+// takes a tile only when its matrix-core GEMV cannot stage the activations
+// in LDS (the lookup kernel then costs 3x the tile at 5..8 rows of 11008
+// inputs).
 bool gemv_uses_gemm_tiles(const LayerDesc &L, int batch) {
-  if (batch < 2 || batch > 8 || !skinny_fits(L, batch, 1)) return false;
+  if (batch < 1 || batch > 8 || !skinny_fits(L, batch, 1)) return false;
+  const bool in_place = L.scheme != Scheme::k2x8 && gemm_mid_direct(L, batch);
   switch (L.scheme) {
     case Scheme::k2x8: return batch >= 3 && !gemv_2x8_mfma_fits(L, batch);
-    case Scheme::k1x16: return (int64_t)batch * L.in >= 32768;
-    case Scheme::k1x16g16: return true;
+    case Scheme::k1x16: return in_place ? batch >= 4 : (int64_t)batch * L.in >= 32768;
+    case Scheme::k1x16g16: return in_place || batch >= 2;
     default: return false;
   }
 }

@@ -132,7 +132,8 @@ AQLM_API int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch
  * instructions with float32 accumulation; W is never written to memory
  * ("AQLM (additive / multi-codebook quantization)", notes: dequantize to
  * float16, then a float16 matrix-engine product). x is [batch][in], y is
- * [batch][out], both float16.
+ * [batch][out], both float16. Up to 8 rows the call runs aqlm_gemv's
+ * routes (the fastest form there) and gives its bits.
  */
 AQLM_API int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
               uint16_t *y, void *stream);

@@ -53,7 +53,8 @@ def test_general_small(scheme, out, J):
 @pytest.mark.parametrize("scheme", [S(4, 8, 8), S(2, 12, 16)], ids=_sid)
 def test_general_one_hot(scheme):
     """x = e_i gives column i of W: exactly for the GEMM (it multiplies the
-    decoded float16 tile), within one float16 ulp for the GEMV."""
+    decoded float16 tile; 16 rows, since up to 8 it runs the GEMV's routes),
+    within one float16 ulp for the GEMV."""
     out, n_in = 200, 48 * scheme.g
     codes, books, scales, _ = WL.small_case(out, n_in, scheme, 1, seed=11)
     layer = dev_layer(codes, books, scales)
@@ -63,7 +64,9 @@ def test_general_one_hot(scheme):
     x[np.arange(len(cols)), cols] = 1
     ref = w_ref[:, cols].T
     # equal as numbers (+0 and -0 compare equal: the zero products may flip a zero's sign)
-    assert np.array_equal(layer.gemm(dev_x(x)).cpu().numpy().astype(np.float32),
+    x16 = np.zeros((16, n_in), dtype=np.float16)
+    x16[:len(cols)] = x
+    assert np.array_equal(layer.gemm(dev_x(x16)).cpu().numpy()[:len(cols)].astype(np.float32),
                           ref.astype(np.float32))
     y = layer.gemv(dev_x(x)).cpu().numpy().astype(np.float32)
     ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float32)

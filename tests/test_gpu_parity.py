@@ -261,7 +261,7 @@ def test_gemv_on_gemm_tiles(sname, out, n_in, batch, tiles):
         assert np.array_equal(bits(y), bits(layer.gemm(dev_x(x), workspace=False)))
 
 
-@pytest.mark.parametrize("batch", [1, 7, 16])
+@pytest.mark.parametrize("batch", [3, 7, 16])
 def test_gemm_one_tile_in_place(batch):
     """Up to 16 rows, on layers with enough row blocks, the product runs one
     activation tile of the workspace form reading x in place: no workspace,
