@@ -688,7 +688,7 @@ bool gemv_uses_gemm_tiles(const LayerDesc &L, int batch) {
   const bool in_place = L.scheme != Scheme::k2x8 && gemm_mid_direct(L, batch);
   switch (L.scheme) {
     case Scheme::k2x8: return batch >= 3 && !gemv_2x8_mfma_fits(L, batch);
-    case Scheme::k1x16: return in_place ? batch >= 4 : (int64_t)batch * L.in >= 32768;
+    case Scheme::k1x16: return in_place ? batch >= 5 : (int64_t)batch * L.in >= 32768;
     case Scheme::k1x16g16: return in_place || batch >= 2;
     default: return false;
   }
