@@ -2,7 +2,8 @@
 benchmark times them) give on every replay exactly the bits of the same calls
 issued eagerly: GEMV (single and grouped), the GEMM with and without its
 workspace (split-K included, the workspace coming from the graph's memory
-pool), and dequant. Eager work runs between the replays, and every replay is
+pool; the one-tile form reading x in place, through the GEMV and the GEMM),
+and dequant. Eager work runs between the replays, and every replay is
 checked. Nothing here clears memory with a memset node: the kernels write
 every output element and the workspace form rewrites its workspace each call.
 """
@@ -24,8 +25,11 @@ def _calls():
     small = dev_layer(c2, b2, sc2)
     c3, b3, sc3, _ = WL.small_case(512, 2048, s2, 1, seed=5)
     third = dev_layer(c3, b3, sc3)
-    xb, xs = dev_x(x), dev_x(x2)
+    c5, b5, sc5, x5 = WL.small_case(7000, 2048, WL.S1x16g16, 16, seed=6)
+    in_place = dev_layer(c5, b5, sc5)                              # one tile, x read in place
+    xb, xs, x16 = dev_x(x), dev_x(x2), dev_x(x5)
     x4 = dev_x(x2[:4])
+    assert in_place.workspace_bytes(16) == 0
     assert big.workspace_bytes(40) > 8192 * 48 * 2 + 512   # the split form is exercised
     outs = {
         "gemv": torch.empty((4, 300), dtype=torch.float16, device=device()),
@@ -35,6 +39,8 @@ def _calls():
         "gemm_ws_small": torch.empty((40, 300), dtype=torch.float16, device=device()),
         "gemm_plain": torch.empty((40, 1000), dtype=torch.float16, device=device()),
         "dequant": torch.empty((300, 2048), dtype=torch.float16, device=device()),
+        "gemv_in_place": torch.empty((4, 7000), dtype=torch.float16, device=device()),
+        "gemm_in_place": torch.empty((16, 7000), dtype=torch.float16, device=device()),
     }
 
     def run():
@@ -44,6 +50,8 @@ def _calls():
         small.gemm(xs, out=outs["gemm_ws_small"])
         big.gemm(xb, out=outs["gemm_plain"], workspace=False)
         small.dequant(out=outs["dequant"])
+        in_place.gemv(x16[:4], out=outs["gemv_in_place"])
+        in_place.gemm(x16, out=outs["gemm_in_place"])
 
     return run, outs, big, xb
 
