@@ -490,6 +490,18 @@ hipError_t launch_group(int cfg, GroupArgs &args, int cus, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Rows per wavefront of gemv_fast_kernel for a layer of `out` rows: the
+// largest of max_rpw, 2, 1 whose grid has at least 2 * kGemvCus workgroups,
+// else 1. The kernel is bound by its codeword gathers per CU, so a short
+// layer (1024 rows at four rows per wavefront is 64 workgroups) must spread
+// its rows over every CU.
+constexpr int kGemvCus = 256;
+inline int fast_rows_per_wave(int out, int max_rpw) {
+  for (int r = max_rpw; r > 1; r /= 2)
+    if ((out + kWaves * r - 1) / (kWaves * r) >= 2 * kGemvCus) return r;
+  return 1;
+}
+
 template <Scheme S, int BATCH>
 hipError_t launch_batch(const LayerDesc &L, const uint16_t *x, uint16_t *y, hipStream_t stream) {
   constexpr int G = group_size(S);
@@ -498,15 +510,25 @@ hipError_t launch_batch(const LayerDesc &L, const uint16_t *x, uint16_t *y, hipS
     if (groups % 8 == 0 && launch_2x8_lds<BATCH>(L, x, y, stream)) return hipGetLastError();
   }
   if (groups % 8 == 0) {
-    constexpr int RPW = BATCH <= 2 ? 4 : 2;
     const int row_chunks = groups / 8;
     int slice_chunks = kXLdsHalves / (BATCH * 8 * G);
     if (slice_chunks < 1) slice_chunks = 1;
-    const int rows_per_block = kWaves * RPW;
+    // Rows per wavefront: the most (4 up to two activation rows, else 2) that
+    // still give two workgroups per CU, else one. A row's sum does not depend
+    // on it, so the result is the same bits whichever is taken.
+    const int rpw = fast_rows_per_wave(out, BATCH <= 2 ? 4 : 2);
+    const int rows_per_block = kWaves * rpw;
     const int grid = (out + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_fast_kernel<S, BATCH, RPW>), dim3(grid), dim3(kBlock), 0, stream,
-                       static_cast<const uint8_t *>(L.codes), L.books, L.scales, x, y, out, in,
-                       row_chunks, slice_chunks);
+    const uint8_t *codes = static_cast<const uint8_t *>(L.codes);
+    if (rpw == 1)
+      hipLaunchKernelGGL((gemv_fast_kernel<S, BATCH, 1>), dim3(grid), dim3(kBlock), 0, stream,
+                         codes, L.books, L.scales, x, y, out, in, row_chunks, slice_chunks);
+    else if (rpw == 2)
+      hipLaunchKernelGGL((gemv_fast_kernel<S, BATCH, 2>), dim3(grid), dim3(kBlock), 0, stream,
+                         codes, L.books, L.scales, x, y, out, in, row_chunks, slice_chunks);
+    else if constexpr (BATCH <= 2)
+      hipLaunchKernelGGL((gemv_fast_kernel<S, BATCH, 4>), dim3(grid), dim3(kBlock), 0, stream,
+                         codes, L.books, L.scales, x, y, out, in, row_chunks, slice_chunks);
   } else {
     int grid = (out + kWaves - 1) / kWaves;
     if (grid > 4096) grid = 4096;

@@ -188,6 +188,21 @@ def test_workload_gemv(wname, lname, batch):
         assert_product(y, y_ref, bound, f"{wname}/{lname} b{batch}")
 
 
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_rows_per_wavefront_same_bits(batch):
+    """The 1x16 GEMV kernel gives each wavefront 1, 2 or 4 rows by the layer's
+    row count (1024, 4096 and 12288 rows here); a row's sum, and so its bits,
+    must not depend on that. The taller layers repeat the 1024-row codes."""
+    c, b, sc, x = WL.small_case(1024, 1024, WL.S1x16, batch, seed=11)
+    y0 = dev_layer(c, b, sc).gemv(dev_x(x)).cpu().numpy()
+    y_ref, bound = oracle.forward(x, c, b, sc)
+    assert_product(y0, y_ref, bound, f"1024 rows b{batch}")
+    for k in (4, 12):
+        yk = dev_layer(np.tile(c, (k, 1, 1)), b, np.tile(sc, k)).gemv(dev_x(x)).cpu().numpy()
+        for i in range(k):
+            assert_bit_exact(yk[:, i * 1024:(i + 1) * 1024], y0, f"{1024 * k} rows, copy {i}")
+
+
 # the workload's batches plus batches of the workspace GEMM (1..16 rows: one
 # activation tile on the 11008-row layers, the skinny tile on the others;
 # 33..128 rows:
