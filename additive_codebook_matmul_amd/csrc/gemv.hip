@@ -490,15 +490,16 @@ hipError_t launch_group(int cfg, GroupArgs &args, int cus, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-// Rows per wavefront of gemv_fast_kernel for a layer of `out` rows: the
-// largest of max_rpw, 2, 1 whose grid has at least 2 * kGemvCus workgroups,
-// else 1. The kernel is bound by its codeword gathers per CU, so a short
-// layer (1024 rows at four rows per wavefront is 64 workgroups) must spread
-// its rows over every CU.
+// Rows per wavefront of gemv_fast_kernel for a layer of `out` rows whose
+// lanes each take `passes` code chunks of a row: the largest of max_rpw, 2, 1
+// for which workgroups x passes reaches 2 * kGemvCus, else 1. The kernel is
+// bound by its codeword gathers per CU, so a short layer (1024 rows at four
+// rows per wavefront is 64 workgroups) must spread its rows over every CU,
+// while rows long enough to give each lane several chunks keep four.
 constexpr int kGemvCus = 256;
-inline int fast_rows_per_wave(int out, int max_rpw) {
+inline int fast_rows_per_wave(int out, int max_rpw, int passes) {
   for (int r = max_rpw; r > 1; r /= 2)
-    if ((out + kWaves * r - 1) / (kWaves * r) >= 2 * kGemvCus) return r;
+    if ((int64_t)((out + kWaves * r - 1) / (kWaves * r)) * passes >= 2 * kGemvCus) return r;
   return 1;
 }
 
@@ -513,10 +514,10 @@ hipError_t launch_batch(const LayerDesc &L, const uint16_t *x, uint16_t *y, hipS
     const int row_chunks = groups / 8;
     int slice_chunks = kXLdsHalves / (BATCH * 8 * G);
     if (slice_chunks < 1) slice_chunks = 1;
-    // Rows per wavefront: the most (4 up to two activation rows, else 2) that
-    // still give two workgroups per CU, else one. A row's sum does not depend
-    // on it, so the result is the same bits whichever is taken.
-    const int rpw = fast_rows_per_wave(out, BATCH <= 2 ? 4 : 2);
+    // Rows per wavefront: 4 (up to two activation rows, else 2), 2 or 1 as
+    // above. A row's sum does not depend on it, so the result is the same
+    // bits whichever is taken.
+    const int rpw = fast_rows_per_wave(out, BATCH <= 2 ? 4 : 2, (row_chunks + 63) / 64);
     const int rows_per_block = kWaves * rpw;
     const int grid = (out + rows_per_block - 1) / rows_per_block;
     const uint8_t *codes = static_cast<const uint8_t *>(L.codes);
