@@ -20,11 +20,13 @@ LIB_PATH = os.path.join(_PKG_DIR, "libaqlm_mi355x.so")
 AQLM_OK = 0
 STATUS_NAMES = {0: "AQLM_OK", 1: "AQLM_ERR_NULL", 2: "AQLM_ERR_SHAPE", 3: "AQLM_ERR_SCHEME",
                 4: "AQLM_ERR_ALIGN", 5: "AQLM_ERR_BATCH", 6: "AQLM_ERR_HIP",
-                7: "AQLM_ERR_WORKSPACE"}
+                7: "AQLM_ERR_WORKSPACE", 8: "AQLM_ERR_SCRATCH"}
 EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemv_batched", "aqlm_gemm",
-                    "aqlm_gemm_workspace_size", "aqlm_gemm_ws", "aqlm_status_string",
-                    "aqlm_abi_version")
-ABI_VERSION = 3
+                    "aqlm_gemm_workspace_size", "aqlm_gemm_ws", "aqlm_gemm_noalloc",
+                    "aqlm_status_string", "aqlm_abi_version")
+ABI_VERSION = 4
+# bytes of the library's static scratch array (AQLM_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 64 << 20
 AQLM_CODES_PACKED = 1
 SCHEMES = {(2, 8, 8): "2x8", (1, 16, 8): "1x16", (1, 16, 16): "1x16g16"}
 
@@ -70,7 +72,7 @@ def load_library() -> ctypes.CDLL:
     lp = ctypes.POINTER(AqlmLayerStruct)
     lib.aqlm_dequant.argtypes = [lp, ctypes.c_void_p, ctypes.c_void_p]
     lib.aqlm_dequant.restype = ctypes.c_int
-    for name in ("aqlm_gemv", "aqlm_gemm"):
+    for name in ("aqlm_gemv", "aqlm_gemm", "aqlm_gemm_noalloc"):
         fn = getattr(lib, name)
         fn.argtypes = [lp, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
@@ -238,6 +240,14 @@ class AqlmLayer:
                                     out.data_ptr(), ws.data_ptr() if ws is not None else None,
                                     need, _stream_handle(self.device)))
         return out
+
+    def gemm_noalloc(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The product of gemm() (aqlm_gemm_ws's kernels and bits) through
+        aqlm_gemm_noalloc, whose scratch memory is the library's static device
+        array: the call allocates nothing on the device (pass `out` to keep
+        the output allocation out of it too). Calls on one GPU that overlap in
+        time race on that array."""
+        return self._product("aqlm_gemm_noalloc", x, out)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         """Pick the lookup path for <= 8 rows and the matrix-core path above."""

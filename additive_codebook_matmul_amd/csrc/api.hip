@@ -2,6 +2,7 @@
 // caller's stream. Nothing here allocates or synchronises.
 #include <limits.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/aqlm.h"
@@ -56,6 +57,36 @@ int from_hip(hipError_t e) { return e == hipSuccess ? AQLM_OK : AQLM_ERR_HIP; }
 
 }  // namespace
 
+// Scratch memory of aqlm_gemm_noalloc: a static device array, one copy per GPU
+// (created when the library's code is loaded on that device, kept until the
+// process ends). In host code `scratch` is only a handle: its device address
+// on each GPU comes from hipGetSymbolAddress, called once per device with
+// that device current, and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[AQLM_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices];  // device address of `scratch` per device, or null
+
+// The current device's scratch address (looked up on the first call there).
+int scratch_address(void **out) {
+  *out = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return AQLM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return AQLM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AQLM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int aqlm_abi_version(void) { return AQLM_ABI_VERSION; }
@@ -72,6 +103,9 @@ const char *aqlm_status_string(int status) {
     case AQLM_ERR_BATCH: return "batch outside the entry point's range";
     case AQLM_ERR_HIP: return "the HIP runtime reported an error";
     case AQLM_ERR_WORKSPACE: return "the workspace is smaller than aqlm_gemm_workspace_size";
+    case AQLM_ERR_SCRATCH: return "the call needs more scratch memory than the library's static "
+                                  "scratch array holds (AQLM_STATIC_SCRATCH_BYTES = 64 MiB); "
+                                  "use aqlm_gemm_ws with a workspace or aqlm_gemm";
     default: return "unknown status";
   }
 }
@@ -160,6 +194,25 @@ int aqlm_gemm_ws(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint
   if (!aligned16(workspace)) return AQLM_ERR_ALIGN;
   if (workspace_bytes < need) return AQLM_ERR_WORKSPACE;
   return from_hip(aqlm::launch_gemm_ws(d, x, batch, y, workspace, s));
+}
+
+int aqlm_gemm_noalloc(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
+                      void *stream) {
+  aqlm::LayerDesc d;
+  const int st = check_layer(layer, &d);
+  if (st != AQLM_OK) return st;
+  if (!gemm_batch_ok(batch)) return AQLM_ERR_BATCH;
+  if (batch == 0) return AQLM_OK;
+  if (!x || !y) return AQLM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return AQLM_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t need = aqlm::gemm_ws_bytes(d, batch);
+  if (need == 0) return from_hip(aqlm::launch_gemm(d, x, batch, y, s));
+  if (need > AQLM_STATIC_SCRATCH_BYTES) return AQLM_ERR_SCRATCH;
+  void *ws = nullptr;
+  const int sst = scratch_address(&ws);
+  if (sst != AQLM_OK) return sst;
+  return from_hip(aqlm::launch_gemm_ws(d, x, batch, y, ws, s));
 }
 
 }  // extern "C"

@@ -55,7 +55,9 @@
  * enqueued and a status below is returned. A launch failure reported by the
  * HIP runtime returns AQLM_ERR_HIP. Faults inside a kernel surface at the
  * caller's next synchronisation. All entry points are reentrant and keep no
- * state. Results are deterministic: the same inputs give bit-identical
+ * state, except aqlm_gemm_noalloc, which keeps the address of its static
+ * scratch array per device and whose overlapping calls on one GPU race (see
+ * there). Results are deterministic: the same inputs give bit-identical
  * outputs on every call.
  */
 #ifndef AQLM_MI355X_H
@@ -67,7 +69,7 @@
 extern "C" {
 #endif
 
-#define AQLM_ABI_VERSION 3
+#define AQLM_ABI_VERSION 4
 
 /* aqlm_layer.flags: codes are bit-packed (see the format above). */
 #define AQLM_CODES_PACKED 1
@@ -87,8 +89,14 @@ typedef enum aqlm_status {
   AQLM_ERR_ALIGN = 4,  /* a pointer is not 16-byte aligned */
   AQLM_ERR_BATCH = 5,  /* batch outside the entry point's range */
   AQLM_ERR_HIP = 6,    /* the HIP runtime reported an error at launch */
-  AQLM_ERR_WORKSPACE = 7 /* the workspace is smaller than aqlm_gemm_workspace_size */
+  AQLM_ERR_WORKSPACE = 7, /* the workspace is smaller than aqlm_gemm_workspace_size */
+  AQLM_ERR_SCRATCH = 8    /* aqlm_gemm_noalloc: the call needs more than
+                             AQLM_STATIC_SCRATCH_BYTES of scratch memory */
 } aqlm_status;
+
+/* Size of the static device scratch array behind aqlm_gemm_noalloc (64 MiB;
+   one copy per GPU the library runs on, held until the process ends). */
+#define AQLM_STATIC_SCRATCH_BYTES (64ll << 20)
 
 /* One quantized layer: sizes plus device pointers to the packed arrays. */
 typedef struct aqlm_layer {
@@ -175,6 +183,29 @@ AQLM_API int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, in
  */
 AQLM_API int aqlm_gemm_ws(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
                           void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * aqlm_gemm_noalloc: aqlm_gemm_ws with no workspace argument and no device
+ * allocation of any kind, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The scratch memory that aqlm_gemm_ws takes from its workspace
+ * comes from a static device array of AQLM_STATIC_SCRATCH_BYTES inside the
+ * library, one per GPU; its address on the current device is looked up on
+ * the first call made on that device (hipGetSymbolAddress) and kept.
+ * Results are bit-identical to aqlm_gemm_ws for the same layer and batch
+ * (the same kernels run). Every call on one GPU shares that GPU's array and
+ * leaves its contents behind: calls on one GPU that may overlap in time
+ * (different streams, or different host threads without ordering) race on
+ * it and must be serialised by the caller. Nothing in the array needs to
+ * start at zero: each call writes every scratch byte it reads. Returns
+ * AQLM_ERR_SCRATCH, with nothing enqueued, when aqlm_gemm_workspace_size for
+ * the layer and batch exceeds AQLM_STATIC_SCRATCH_BYTES (call aqlm_gemm_ws
+ * with a workspace, or aqlm_gemm, instead), AQLM_ERR_HIP if the array's
+ * address cannot be obtained; otherwise as aqlm_gemm. Device ordinals must
+ * be below 64.
+ */
+AQLM_API int aqlm_gemm_noalloc(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
+                               uint16_t *y, void *stream);
 
 /*
  * aqlm_gemv_batched: aqlm_gemv for num_layers independent layers in one call:

@@ -51,8 +51,8 @@ def test_struct_layout_matches_header():
 
 
 def test_status_strings():
-    for st in range(8):
-        assert _lib.status_string(st)
+    for st in range(9):
+        assert _lib.status_string(st) != "unknown status"
     assert _lib.status_string(99) == "unknown status"
     assert _lib.status_string(0) == "ok"
 
@@ -67,6 +67,7 @@ ENTRY = {
     "aqlm_gemm": lambda s, x, b, y: _lib.raw_call("aqlm_gemm", s, x, b, y, None),
     "aqlm_gemm_ws": lambda s, x, b, y: _lib.raw_call("aqlm_gemm_ws", s, x, b, y, FAKE, 1 << 40,
                                                      None),
+    "aqlm_gemm_noalloc": lambda s, x, b, y: _lib.raw_call("aqlm_gemm_noalloc", s, x, b, y, None),
 }
 
 
@@ -104,7 +105,7 @@ def test_output_pointer_validation(fn):
     assert ENTRY[fn](s, FAKE, 1, MISALIGNED) == 4
 
 
-@pytest.mark.parametrize("fn", ["aqlm_gemv", "aqlm_gemm", "aqlm_gemm_ws"])
+@pytest.mark.parametrize("fn", ["aqlm_gemv", "aqlm_gemm", "aqlm_gemm_ws", "aqlm_gemm_noalloc"])
 def test_input_pointer_and_batch_validation(fn):
     s = _layer()
     assert ENTRY[fn](s, 0, 1, FAKE) == 1
@@ -119,6 +120,7 @@ def test_batch_limits():
     assert ENTRY["aqlm_gemv"](s, FAKE, 9, FAKE) == 5
     assert ENTRY["aqlm_gemm"](s, FAKE, 1 << 40, FAKE) == 5
     assert ENTRY["aqlm_gemm_ws"](s, FAKE, 1 << 40, FAKE) == 5
+    assert ENTRY["aqlm_gemm_noalloc"](s, FAKE, 1 << 40, FAKE) == 5
 
 
 def _ws_size(s, batch):
@@ -167,6 +169,26 @@ def test_workspace_validation():
     assert f(ctypes.byref(s), FAKE, 64, FAKE, MISALIGNED, need, None) == 4
     assert f(ctypes.byref(s), FAKE, 64, FAKE, FAKE, need - 1, None) == 7
     assert f(ctypes.byref(s), FAKE, 0, FAKE, None, 0, None) == 0     # batch 0: no-op
+
+
+def test_noalloc_rejects_calls_beyond_the_static_scratch():
+    """aqlm_gemm_noalloc returns AQLM_ERR_SCRATCH, before any launch, when the
+    workspace form would need more than the static scratch array holds."""
+    f = _lib.load_library().aqlm_gemm_noalloc
+    big = None
+    for out, n_in in ((1024, 28672), (1024, 65536)):
+        for batch in (1000, 2000):
+            s = _layer(out=out, n_in=n_in)
+            st, need = _ws_size(s, batch)
+            if st == 0 and need > _lib.STATIC_SCRATCH_BYTES:
+                big = (s, batch)
+                break
+        if big:
+            break
+    assert big is not None, "no shape needs more than the static scratch"
+    s, batch = big
+    assert f(ctypes.byref(s), FAKE, batch, FAKE, None) == 8
+    assert "64 MiB" in _lib.status_string(8)
 
 
 def test_binding_rejects_cpu_tensors_without_calling_the_library():
