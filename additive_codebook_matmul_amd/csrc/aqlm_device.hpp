@@ -98,6 +98,46 @@ __device__ __forceinline__ uint4 hadd8(const uint4 &a, const uint4 &b) {
   return make_uint4(hadd2(a.x, b.x), hadd2(a.y, b.y), hadd2(a.z, b.z), hadd2(a.w, b.w));
 }
 
+// Overflow guard of the fp16 codeword sum in the 2x8 matrix-core tiles.
+// Those tiles feed fp16(C_0[c_0] + C_1[c_1]) to the matrix cores and apply the
+// row scale to the float32 total. The fp16 sum overflows when both codewords
+// are large (|C_0 + C_1| > 65504) even where the decoded weight
+// s * (C_0 + C_1) is finite (|s| < 1); it cannot when every codebook half is
+// below 2^15 in magnitude, since the largest such value is 32752 and
+// 2 * 32752 = 65504. A workgroup whose staged codebooks hold a half of
+// magnitude >= 2^15 (infinities and NaNs included) halves every codeword in
+// its table (exact for normal values; subnormal halves round to nearest
+// even) and doubles its float32 partial sums before the scale (exact).
+//
+// True when some fp16 half of v has magnitude >= 2^15: (bits & 0x7FFF) +
+// 0x0800 reaches bit 15 exactly then, with no carry between the halves.
+__device__ __forceinline__ bool has_large_half(const uint4 &v) {
+  const uint32_t m = 0x7FFF7FFFu, k = 0x08000800u;
+  return ((((v.x & m) + k) | ((v.y & m) + k) | ((v.z & m) + k) | ((v.w & m) + k)) &
+          0x80008000u) != 0;
+}
+// Every half of a codeword times 0.5 (packed fp16 multiplies, round to
+// nearest even).
+__device__ __forceinline__ uint32_t hhalf2(uint32_t a) {
+  const half2_t h = {(_Float16)0.5f, (_Float16)0.5f};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * h);
+}
+__device__ __forceinline__ uint4 hhalf8(const uint4 &a) {
+  return make_uint4(hhalf2(a.x), hhalf2(a.y), hhalf2(a.z), hhalf2(a.w));
+}
+// Workgroup OR of a per-thread flag around a barrier the caller already has:
+// publish_flag before it (one LDS word per wavefront, flags[wave]), read_flag
+// after it. The result is uniform across the workgroup.
+__device__ __forceinline__ void publish_flag(uint32_t *flags, bool mine) {
+  const uint64_t b = __ballot(mine);
+  if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = b != 0 ? 1u : 0u;
+}
+__device__ __forceinline__ bool read_flag(const uint32_t *flags, int waves) {
+  uint32_t f = 0;
+  for (int w = 0; w < waves; ++w) f |= flags[w];
+  return __builtin_amdgcn_readfirstlane(f) != 0;
+}
+
 // Pins a float32 value in a register: the optimiser may not fold the
 // operation that produced it into a later one. Without it, fp16(a * s) is
 // compiled to v_fma_mixlo_f16(a, s, +0), which rounds the exact product once

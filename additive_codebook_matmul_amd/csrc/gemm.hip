@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kBlock) void gemm_wide_kernel(
   constexpr int KD = kWideCodeDepth;
   __shared__ uint4 lds_books[S == Scheme::k2x8 ? 512 : 1];
   __shared__ __attribute__((aligned(16))) uint16_t lds_x[2][C::TILE_HALVES];
+  __shared__ uint32_t big_flags[kBlock / 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -228,10 +229,26 @@ __global__ __launch_bounds__(kBlock) void gemm_wide_kernel(
   load_x(0, xr[0]);
   load_x(1, xr[1]);
   if constexpr (S == Scheme::k2x8) {
-    for (int i = threadIdx.x; i < 512; i += kBlock) lds_books[i] = gbooks[i];
+    bool large = false;
+    for (int i = threadIdx.x; i < 512; i += kBlock) {
+      const uint4 v = gbooks[i];
+      large |= has_large_half(v);
+      lds_books[i] = v;
+    }
+    publish_flag(big_flags, large);
   }
   store_x(0, xr[0]);
   __syncthreads();
+  // codebooks large enough for the fp16 codeword sum to overflow: halve the
+  // table, double the totals (overflow guard, aqlm_device.hpp)
+  float total_mul = 1.0f;
+  if constexpr (S == Scheme::k2x8) {
+    if (read_flag(big_flags, kBlock / 64)) {
+      for (int i = threadIdx.x; i < 512; i += kBlock) lds_books[i] = hhalf8(lds_books[i]);
+      __syncthreads();
+      total_mul = 2.0f;
+    }
+  }
 
   const bool tail_partial = groups % kKG != 0;
   // K block kb (code slot K = kb % KD, activation slot kb % 2): prefetch
@@ -271,7 +288,8 @@ __global__ __launch_bounds__(kBlock) void gemm_wide_kernel(
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (row < out)
-          y[(int64_t)tok * out + row] = (uint16_t)f2h(acc[mi][ni][r] * h2f(scales[row]));
+          y[(int64_t)tok * out + row] =
+              (uint16_t)f2h((acc[mi][ni][r] * total_mul) * h2f(scales[row]));
       }
     }
   }
@@ -309,11 +327,12 @@ constexpr int kSkinnyCodeDepth = 4;  // the step loop below is unrolled to match
 constexpr int64_t kSkinnyMaxBatch = 128;  // above this the wide tiles take over
 constexpr int kSkinnyXSlotBytes = 16 * 512;  // one 16-row activation tile of a chunk
 
-// Dynamic LDS of one block: [2x8 codebooks 8 KiB][code transpose 1 KiB per
-// wave][activation slots NT x 8 KiB per wave]; the final reduction reuses the
-// activation slots.
+// Dynamic LDS of one block: [2x8 codebooks 8 KiB, overflow-guard flags 64 B]
+// [code transpose 1 KiB per wave][activation slots NT x 8 KiB per wave]; the
+// final reduction reuses the activation slots.
+constexpr int kSkinnyBooksBytes = 8192 + 64;
 constexpr int skinny_lds_bytes(bool lut, int nt, int waves) {
-  return (lut ? 8192 : 0) + waves * 1024 + waves * nt * kSkinnyXSlotBytes;
+  return (lut ? kSkinnyBooksBytes : 0) + waves * 1024 + waves * nt * kSkinnyXSlotBytes;
 }
 
 template <Scheme S, int NT, bool ALIGNED>
@@ -340,7 +359,8 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void gemm_skinny_kernel(
   const uint4 *gbooks = reinterpret_cast<const uint4 *>(books);
 
   uint4 *lds_books = reinterpret_cast<uint4 *>(lds);
-  uint8_t *lds_codes = lds + (LUT ? 8192 : 0);
+  uint32_t *big_flags = reinterpret_cast<uint32_t *>(lds + 8192);
+  uint8_t *lds_codes = lds + (LUT ? kSkinnyBooksBytes : 0);
   uint8_t *lds_xall = lds_codes + waves * 1024;
   uint4 *xslot = reinterpret_cast<uint4 *>(lds_xall + wave * NT * kSkinnyXSlotBytes);
   uint16_t *cslot = reinterpret_cast<uint16_t *>(lds_codes + wave * 1024) + r * 32;
@@ -480,10 +500,24 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void gemm_skinny_kernel(
 #pragma unroll
     for (int i = 0; i < CD; ++i) load_codes(chunk_of(i), cw[i]);
   }
+  bool halved = false;
   if constexpr (LUT) {
     // issued after the first chunk's loads so that the latencies overlap
-    for (int i = threadIdx.x; i < 512; i += blockDim.x) lds_books[i] = gbooks[i];
+    bool large = false;
+    for (int i = threadIdx.x; i < 512; i += blockDim.x) {
+      const uint4 v = gbooks[i];
+      large |= has_large_half(v);
+      lds_books[i] = v;
+    }
+    publish_flag(big_flags, large);
     __syncthreads();
+    // codebooks large enough for the fp16 codeword sum to overflow: halve the
+    // table, double the totals (overflow guard, aqlm_device.hpp)
+    halved = read_flag(big_flags, waves);
+    if (halved) {
+      for (int i = threadIdx.x; i < 512; i += blockDim.x) lds_books[i] = hhalf8(lds_books[i]);
+      __syncthreads();
+    }
   }
   if (nmain > 0) {
     store_x(xr);
@@ -529,6 +563,10 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void gemm_skinny_kernel(
     compute(std::true_type{}, c, tsc, ga[0]);
   }
 
+  if (halved) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = acc[t] * 2.0f;
+  }
   // Epilogue: add the waves' partial sums in wave order, scale, round.
   auto write = [&](int t, int l, const float4_t &v) {
     const int tok = tok0 + 16 * t + (l & 15);

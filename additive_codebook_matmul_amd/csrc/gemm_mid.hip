@@ -83,10 +83,11 @@ struct MidCfg {
 constexpr int ring_depth(int rt, int nt) { return rt * nt >= 16 ? 2 : rt * nt >= 8 ? 4 : 8; }
 
 // LDS: the 2x8 table (reused for the partial tiles after the K loop), then
-// the row scales
+// the row scales, then one overflow-guard flag per wavefront
 constexpr size_t mid_red_bytes(int rt, int nt) { return (size_t)kMidWaves * rt * nt * 1024; }
 constexpr size_t mid_lds_bytes(bool lut, int rt, int nt) {
-  return ((lut && mid_red_bytes(rt, nt) < 65536) ? 65536 : mid_red_bytes(rt, nt)) + 64 * 4;
+  return ((lut && mid_red_bytes(rt, nt) < 65536) ? 65536 : mid_red_bytes(rt, nt)) + 64 * 4 +
+         kMidWaves * 4;
 }
 
 // Code of step s (a compile-time constant) from a lane's 16 code bytes: g = 8
@@ -195,7 +196,9 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *table = lds;
   float4_t *red = reinterpret_cast<float4_t *>(lds);
-  float *lds_scale = reinterpret_cast<float *>(lds + mid_lds_bytes(LUT, RT, NT) - 64 * 4);
+  uint32_t *big_flags = reinterpret_cast<uint32_t *>(lds + mid_lds_bytes(LUT, RT, NT) -
+                                                     kMidWaves * 4);
+  float *lds_scale = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(big_flags) - 64 * 4);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -319,6 +322,7 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
   uint4 bx[D][NT];
   uint4 ga[LUT ? 1 : D][RT];
   uint4 a[2][RT];
+  bool halved = false;  // overflow guard of the 2x8 codeword sum
   load_codes(sc, cw[0]);
   load_codes(sc + kMidWaves, cw[1]);
 #pragma unroll
@@ -336,7 +340,21 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
       *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + slot) = v0;
       *reinterpret_cast<uint4 *>(table + (tc + 128) * 256 + tm * 128 + slot) = v1;
     }
+    publish_flag(big_flags, has_large_half(v0) || has_large_half(v1));
     __syncthreads();
+    // codebooks large enough for the fp16 codeword sum to overflow: halve the
+    // table, double the totals (overflow guard, aqlm_device.hpp)
+    halved = read_flag(big_flags, kMidWaves);
+    if (halved) {
+      const uint4 h0 = hhalf8(v0), h1 = hhalf8(v1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int slot = ((j + tid) & 7) * 16;
+        *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + slot) = h0;
+        *reinterpret_cast<uint4 *>(table + (tc + 128) * 256 + tm * 128 + slot) = h1;
+      }
+      __syncthreads();
+    }
     decode(cw[0], 0, a[0]);
   } else {
 #pragma unroll
@@ -412,6 +430,12 @@ void gemm_mid_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restri
     super_chunk(std::integral_constant<int, 1>{});
   }
 
+  if (halved) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[t][j] = acc[t][j] * 2.0f;
+  }
   // the four wavefronts' partial tiles, added in wavefront order (the 2x8
   // table is dead once every wavefront has left the K loop)
   if constexpr (LUT) __syncthreads();

@@ -46,10 +46,11 @@ constexpr uint32_t kMOOB = 0x80000000u;
 
 // LDS: the 64 KiB table is a static array (its addresses then fold into the
 // read instructions); the dynamic part holds the activations (BATCH rows of
-// in + 8 halves), the row scales and the reduction buffers (two of waves x 16
-// rows x BATCH floats).
+// in + 8 halves), the row scales, the reduction buffers (two of waves x 16
+// rows x BATCH floats) and one overflow-guard flag per wavefront.
 constexpr size_t mfma_dyn_lds_bytes(int batch, int in) {
-  return (size_t)batch * (in + 8) * 2 + kMaxTilesPerBlock * 16 * 2 + 2 * kMWaves * 16 * batch * 4;
+  return (size_t)batch * (in + 8) * 2 + kMaxTilesPerBlock * 16 * 2 + 2 * kMWaves * 16 * batch * 4 +
+         kMWaves * 4;
 }
 constexpr size_t mfma_lds_bytes(int batch, int in) { return kMTable + mfma_dyn_lds_bytes(batch, in); }
 
@@ -72,6 +73,7 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
   uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
   uint16_t *sc_lds = xs + BATCH * xstride;
   float *red = reinterpret_cast<float *>(sc_lds + kMaxTilesPerBlock * 16);
+  uint32_t *big_flags = reinterpret_cast<uint32_t *>(red + 2 * kMWaves * 16 * BATCH);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,7 +175,19 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
   // B fragments: activation row min(r, batch - 1) (columns past the batch
   // repeat the last row and are never stored)
   const uint16_t *xrow = xs + (r < batch ? r : batch - 1) * xstride + (cb * 32 + q * 8) * 8;
+  publish_flag(big_flags, has_large_half(book_v));
   __syncthreads();
+  // codebooks large enough for the fp16 codeword sum to overflow: halve the
+  // table, double the row totals (overflow guard, aqlm_device.hpp)
+  const bool halved = read_flag(big_flags, kMWaves);
+  if (halved) {
+    const uint4 hv = hhalf8(book_v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + ((j + tid) & 7) * 16) = hv;
+    __syncthreads();
+  }
+  const float total_mul = halved ? 2.0f : 1.0f;
 
   auto tile = [&](int i, const uint4 (&c)[MAXC]) {
     float4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -223,7 +237,7 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
       for (int w2 = 1; w2 < kMWaves; ++w2) v += rb[(w2 * 16 + row16) * BATCH + b];
       const int row = (blk + i * L.blk_count) * 16 + row16;
       if (row < out && b < batch)
-        L.y[(int64_t)b * out + row] = (uint16_t)f2h(v * h2f(sc_lds[i * 16 + row16]));
+        L.y[(int64_t)b * out + row] = (uint16_t)f2h((v * total_mul) * h2f(sc_lds[i * 16 + row16]));
     }
   };
 

@@ -4,8 +4,10 @@ Decoded weights (aqlm_dequant) must match bit for bit; products (aqlm_gemv,
 aqlm_gemm) must lie within 1e-2 * sum_i |x_i w_i| of the float64 oracle for
 every output, and within the tighter 1e-3 gate. Sizes: small ragged layers
 that span several tiles and a tail, and every layer of the five workloads at
-full size (the 70B-shaped layers on sampled rows, the 2048-row products on
-sampled activation rows).
+full size on every row (the 70B-shaped layers in chunks of 2048 rows, the
+2048-row products on sampled activation rows). One-hot probes (64 columns per
+workload layer, group edges and row tails included) check single columns of W
+to within one float16 ulp, which the loose tolerance cannot.
 """
 import functools
 import json
@@ -149,8 +151,8 @@ def _sample_rows(out, n=1024, seed=0):
     return rows[(rows >= 0) & (rows < out)]
 
 
-LAYER_IDS = [(w.name, l.name) for w in WL.WORKLOADS.values() for l in w.layers]
-BIG = {"llama2_70b_1x16"}  # oracle on sampled rows
+BIG = "llama2_70b_1x16"  # layers of up to 235 M weights: checked in row chunks below
+LAYER_IDS = [(w.name, l.name) for w in WL.WORKLOADS.values() for l in w.layers if w.name != BIG]
 
 
 @pytest.mark.parametrize("wname,lname", LAYER_IDS, ids=lambda v: str(v))
@@ -158,19 +160,13 @@ def test_workload_dequant_bit_exact(wname, lname):
     layer, d = _layer_data(wname, lname)
     gl = dev_layer(d.codes, d.codebooks, d.scales)
     w = gl.dequant()
-    if wname in BIG:
-        rows = _sample_rows(layer.out_features)
-        w_rows = w[torch.from_numpy(rows).to(device())].cpu().numpy()
-        ref = oracle.decode_rows(d.codes, d.codebooks, d.scales, rows)
-        assert_bit_exact(w_rows, ref, f"{wname}/{lname} sampled rows")
-    else:
-        assert_bit_exact(w.cpu().numpy(), oracle.decode(d.codes, d.codebooks, d.scales),
-                         f"{wname}/{lname}")
+    assert_bit_exact(w.cpu().numpy(), oracle.decode(d.codes, d.codebooks, d.scales),
+                     f"{wname}/{lname}")
     del w
     torch.cuda.empty_cache()
 
 
-GEMV_IDS = [(w.name, l.name, b) for w in WL.WORKLOADS.values() if w.index <= 4
+GEMV_IDS = [(w.name, l.name, b) for w in WL.WORKLOADS.values() if w.index <= 4 and w.name != BIG
             for l in w.layers for b in w.batches]
 
 
@@ -179,13 +175,82 @@ def test_workload_gemv(wname, lname, batch):
     layer, d = _layer_data(wname, lname)
     x = WL.make_x(layer, batch)
     y = dev_layer(d.codes, d.codebooks, d.scales).gemv(dev_x(x)).cpu().numpy()
-    if wname in BIG:
-        rows = _sample_rows(layer.out_features)
-        y_ref, bound = oracle.forward_rows(x, d.codes, d.codebooks, d.scales, rows)
-        assert_product(y[:, rows], y_ref, bound, f"{wname}/{lname} b{batch}")
-    else:
-        y_ref, bound = oracle.forward(x, d.codes, d.codebooks, d.scales)
-        assert_product(y, y_ref, bound, f"{wname}/{lname} b{batch}")
+    y_ref, bound = oracle.forward(x, d.codes, d.codebooks, d.scales)
+    assert_product(y, y_ref, bound, f"{wname}/{lname} b{batch}")
+
+
+def _probe_columns(n_in, g, n=64, seed=0):
+    """n input columns for one-hot probes: the first and last column of the
+    first, second and middle groups, the row tail (the last group whole), and
+    seeded random columns for the rest."""
+    J = n_in // g
+    fixed = [0, g - 1, g, 2 * g - 1, (J // 2) * g, (J // 2) * g + g - 1]
+    fixed += list(range(n_in - g, n_in))
+    fixed = sorted(set(c for c in fixed if 0 <= c < n_in))
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(n_in), fixed)
+    extra = rng.choice(rest, size=max(0, min(n, n_in) - len(fixed)), replace=False)
+    return np.sort(np.concatenate([fixed, extra]).astype(np.int64))
+
+
+def _one_hot_check(L, cols, ref_cols, what):
+    """x = e_c for every probe column c: y[:, o] must be W16[o, c] to within one
+    float16 ulp, through the GEMV (8 columns per call) and through the GEMM's
+    matrix-core tiles (all columns in one call, with and without a workspace)."""
+    n_in = L.in_features
+    x = np.zeros((len(cols), n_in), dtype=np.float16)
+    x[np.arange(len(cols)), cols] = 1
+    ref = ref_cols.T.astype(np.float32)  # [len(cols), out]
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float32)
+    for b0 in range(0, len(cols), 8):
+        y = L.gemv(dev_x(x[b0:b0 + 8])).cpu().numpy().astype(np.float32)
+        bad = np.abs(y - ref[b0:b0 + 8]) > ulp[b0:b0 + 8]
+        assert not bad.any(), f"{what} gemv: column {cols[b0 + np.argwhere(bad)[0][0]]}"
+    if not L.general:
+        for ws in (True, False):
+            y = L.gemm(dev_x(x), workspace=ws).cpu().numpy().astype(np.float32)
+            bad = np.abs(y - ref) > ulp
+            assert not bad.any(), f"{what} gemm ws={ws}: column {cols[np.argwhere(bad)[0][0]]}"
+
+
+ONE_HOT_IDS = [(w.name, l.name) for w in WL.WORKLOADS.values() if w.name != BIG
+               for l in w.layers if not l.packed]
+
+
+@pytest.mark.parametrize("wname,lname", ONE_HOT_IDS, ids=lambda v: str(v))
+def test_workload_one_hot_probes(wname, lname):
+    """64 one-hot probes per workload layer, including the first and last
+    column of groups and the row tail: the loose product tolerance cannot see
+    a single dropped or misplaced group at these widths, these probes can."""
+    layer, d = _layer_data(wname, lname)
+    cols = _probe_columns(layer.in_features, layer.scheme.g, seed=layer.seed)
+    ref = oracle.decode(d.codes, d.codebooks, d.scales)[:, cols]
+    _one_hot_check(dev_layer(d.codes, d.codebooks, d.scales), cols, ref, f"{wname}/{lname}")
+
+
+@pytest.mark.parametrize("lname", [l.name for l in WL.WORKLOADS[BIG].layers])
+def test_llama2_70b_layer_every_row(lname):
+    """The Llama-2-70B-shaped layers checked on every row, in chunks of 2048
+    rows (one oracle decode pass per layer): aqlm_dequant bit-exact, aqlm_gemv
+    at batch 1 within tolerance, and 64 one-hot probes."""
+    layer, d = _layer_data(BIG, lname)
+    out = layer.out_features
+    L = dev_layer(d.codes, d.codebooks, d.scales)
+    w_gpu = L.dequant()
+    x = WL.make_x(layer, 1)
+    y_gpu = L.gemv(dev_x(x)).cpu().numpy()
+    cols = _probe_columns(layer.in_features, layer.scheme.g, seed=layer.seed)
+    ref_cols = np.empty((out, len(cols)), dtype=np.float16)
+    for r0 in range(0, out, 2048):
+        rows = np.arange(r0, min(out, r0 + 2048))
+        ref = oracle.decode_rows(d.codes, d.codebooks, d.scales, rows)
+        assert_bit_exact(w_gpu[r0:r0 + len(rows)].cpu().numpy(), ref, f"{BIG}/{lname} rows {r0}+")
+        y_ref, bound = oracle.product(x, ref)
+        assert_product(y_gpu[:, rows], y_ref, bound, f"{BIG}/{lname} gemv rows {r0}+")
+        ref_cols[rows] = ref[:, cols]
+    del w_gpu
+    torch.cuda.empty_cache()
+    _one_hot_check(L, cols, ref_cols, f"{BIG}/{lname}")
 
 
 @pytest.mark.parametrize("batch", [1, 4])
