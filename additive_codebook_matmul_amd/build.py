@@ -3,7 +3,9 @@
 Usage: python -m additive_codebook_matmul_amd.build   (or call build_library()).
 The library lands next to this file as libaqlm_mi355x.so; objects go under
 _build/. Every call recompiles from source. build_host_library() compiles the
-separate host GEMV library (libaqlm_host.so, g++ with OpenMP).
+separate host GEMV library (libaqlm_host.so, g++ with OpenMP);
+build_ceiling_library() the benchmark's measurement kernels
+(libaqlm_ceiling.so).
 """
 from __future__ import annotations
 
@@ -25,6 +27,10 @@ SOURCES = ("api.hip", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "g
 ARCH = "gfx950"
 HOST_SOURCE = "host_gemv.cpp"
 HOST_LIB_PATH = os.path.join(PKG_DIR, "libaqlm_host.so")
+# measurement kernels of the benchmark (read and gather ceilings), a library
+# of their own so that the product library exports only its C-ABI
+CEILING_SOURCE = "ceiling.hip"
+CEILING_LIB_PATH = os.path.join(PKG_DIR, "libaqlm_ceiling.so")
 
 
 def hipcc() -> str:
@@ -82,6 +88,19 @@ def build_host_library(verbose: bool = True) -> str:
     return HOST_LIB_PATH
 
 
+def build_ceiling_library(verbose: bool = True) -> str:
+    tmp = CEILING_LIB_PATH + ".tmp"
+    cmd = [hipcc(), *compile_flags(), "-shared", os.path.join(CSRC, CEILING_SOURCE), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"ceiling library build failed:\n{res.stderr}")
+    os.replace(tmp, CEILING_LIB_PATH)
+    if verbose:
+        print(f"built {CEILING_LIB_PATH}", file=sys.stderr)
+    return CEILING_LIB_PATH
+
+
 if __name__ == "__main__":
     build_library()
     build_host_library()
+    build_ceiling_library()

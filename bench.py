@@ -1,32 +1,40 @@
-"""Benchmark: batch-1 AQLM GEMV over the Llama-2-7B linear-layer set (scheme 2x8).
+"""Benchmark: batch-1 AQLM GEMV over Llama-2-7B-shaped linear layers.
 
-One step = the seven Llama-2-7B linear layers of one transformer block
-(q, k, v, o: 4096x4096; gate, up: 11008x4096; down: 4096x11008), scheme 2x8
-(two 8-bit codebooks, codeword length 8), one activation row, seeded
-synthetic weights, issued the way a decode step can issue them: q, k and v
-share their input and go out as one aqlm_gemv_batched call, then o, then gate
-and up (shared input) as one batched call, then down. The codes, scales,
-activations and outputs are rotated over enough distinct copies (>= 1 GiB of
-codes) that every step reads its codes from HBM, not from the 256 MiB
-last-level cache; the 8 KiB codebooks are shared.
+One step is one decode token through the linear layers of Llama-2-7B: 32
+transformer blocks of seven layers each (q, k, v, o: 4096x4096; gate, up:
+11008x4096; down: 4096x11008), batch 1, seeded synthetic weights. Each block
+has its own copy of the codes and scales in HBM (32 distinct buffers of the
+seeded block, 1.54 GB of codes per step, far above the 256 MiB last-level
+cache), so every step reads its codes from HBM; the codebooks are shared, as
+the workload statement puts them in L2. A block issues its layers the way a
+decode step can: q, k and v share their input and go out as one
+aqlm_gemv_batched call, then o, then gate and up (shared input) as one
+batched call, then down. The step is captured once as a HIP graph; the timed
+region is exactly --steps replays of it, bracketed by device synchronisation
+and timed with HIP events on the replay stream.
 
-Reported value: achieved HBM GB/s = (codes + x + y bytes of the seven layers)
-/ time per step, timed with HIP events on the stream the kernels run on,
-bracketed by device synchronisation. Also reported: microseconds per layer
-launched alone, the whole block as a single batched call, the roofline
-object of the dominant kernel (the grouped GEMV of the q,k,v and gate,up
-calls), the CPU oracle timed on a bounded sample of the same workload, and
-the host library's GEMV (aqlm_host_gemv, table lookup on the CPU cores) on the
-same seven layers.
+Reported value: achieved HBM GB/s of the scheme-2x8 step (two 8-bit
+codebooks, codeword length 8) = (codes + x + y bytes of the 224 layers) /
+time per step. The same step is measured for scheme 1x16 (one 16-bit
+codebook of 1 MiB) under "schemes", with its own roofline object. Also
+reported, per scheme: microseconds per layer and per call, the block as one
+batched call, and the roofline of the dominant kernel; for context: the
+pure-read and random-gather ceilings measured here with the benchmark's own
+kernels (libaqlm_ceiling.so), dense float16 torch.nn.functional.linear at the
+same shapes, the CPU oracle on a bounded sample (decode and product timed
+separately), and the host library's GEMV.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --workload NAME   (per-layer tables of the other workloads)
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -37,22 +45,51 @@ if ROOT not in sys.path:
 METRIC = "AQLM GEMV µs/layer + achieved HBM GB/s (% of peak), Llama-2-7B shapes, batch 1"
 WORKLOAD = "llama2_7b_2x8"
 HBM_PEAK_GBPS = 8000.0
+CLOCK_GHZ = 2.4  # MI355X peak engine clock, for per-clock rates
 ROTATE_BYTES = 1 << 30
-GEMV_KERNEL = "gemv_2x8_mfma_group_kernel (grouped 2x8 GEMV on the matrix cores, batch 1)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_2x8_llama2_7b_b1_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "additive_codebook_matmul_amd", "csrc", "gemv_mfma.hip")
+MODEL_BLOCKS = 32  # transformer blocks of Llama-2-7B
+CALLS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
+CSRC = os.path.join(ROOT, "additive_codebook_matmul_amd", "csrc")
+CEILING_LIB = os.path.join(ROOT, "additive_codebook_matmul_amd", "libaqlm_ceiling.so")
+
+# Per scheme: the workload, the launches that make up its dominant kernel (a
+# call of several layers is one grouped launch where the grouped kernel serves
+# it), that kernel's name and source, and the HBM counter summary of it.
+SCHEME_SPECS = {
+    "2x8": {
+        "workload": "llama2_7b_2x8",
+        "scheme": "2x8 (M=2, B=8, g=8)",
+        "kernel": "gemv_2x8_mfma_group_kernel (grouped 2x8 GEMV on the matrix cores, batch 1)",
+        "dominant": (("q", "k", "v"), ("gate", "up")),
+        "source": "gemv_mfma.hip",
+        "traffic": os.path.join(ROOT, "profiles", "gemv_2x8_llama2_7b_b1_traffic.json"),
+    },
+    "1x16": {
+        "workload": "llama2_7b_1x16",
+        "scheme": "1x16 (M=1, B=16, g=8, 1 MiB codebook)",
+        "kernel": "gemv_fast_kernel<1x16> (codeword gathers through L2, batch 1)",
+        "dominant": (("q",), ("k",), ("v",), ("o",), ("gate",), ("up",), ("down",)),
+        "source": "gemv.hip",
+        "traffic": os.path.join(ROOT, "profiles", "gemv_1x16_llama2_7b_b1_traffic.json"),
+    },
+}
 
 
 def _parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=20,
+                   help="timed steps (one step: 32 blocks x 7 layers, one token)")
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--layer-iters", type=int, default=200,
-                   help="launches per layer for the per-layer timing")
+                   help="launches per layer for the per-layer tables of --workload")
+    p.add_argument("--schemes", default="2x8,1x16",
+                   help="schemes of the headline run (2x8 is the reported value)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-host-gemv", action="store_true",
                    help="skip timing the host library's GEMV on the CPU cores")
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the ceilings and the dense float16 comparator")
     p.add_argument("--workload", default=WORKLOAD,
                    help="llama2_7b_2x8 (default: the headline step), or per-layer tables for "
                         "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, "
@@ -61,6 +98,68 @@ def _parse():
                    help="only run device-to-device copies of MIB MiB (for scaling the HBM "
                         "byte counters of a profiler) and exit")
     return p.parse_args()
+
+
+def _source_hash(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(spec):
+    """HBM bytes per launch from rocprofv3 counters, if taken on this kernel source."""
+    try:
+        with open(spec["traffic"]) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != _source_hash(spec["source"]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _median_time(fn, runs=3):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts)
+
+
+def cpu_baseline(layers_np):
+    """The CPU oracle on the seven layers of one block: O1 decode (numpy,
+    float32, single-threaded) and O2 product (float64 BLAS) timed separately
+    per layer, median of three runs each."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the interpreter's one thread
+        blas_threads = 1
+    t_dec = t_prod = 0.0
+    block_bytes = 0
+    t0 = time.perf_counter()
+    per_layer = {}
+    for (layer, d, x, nbytes) in layers_np:
+        w = oracle.decode(d.codes, d.codebooks, d.scales)
+        td = _median_time(lambda: oracle.decode(d.codes, d.codebooks, d.scales))
+        tp = _median_time(lambda: oracle.product(x, w))
+        t_dec += td
+        t_prod += tp
+        block_bytes += nbytes
+        per_layer[layer.name] = {"decode_ms": round(1e3 * td, 1), "product_ms": round(1e3 * tp, 1)}
+    wall = time.perf_counter() - t0
+    return {
+        "value": round(block_bytes / (t_dec + t_prod) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"one Llama-2-7B block (seven layers, batch 1) of the scheme: O1 decode "
+                  f"{1e3 * t_dec:.0f} ms, O2 product {1e3 * t_prod:.0f} ms per block, each the "
+                  f"median of 3 runs per layer ({wall:.1f} s in all); decode is single-threaded "
+                  f"numpy, the float64 product uses BLAS with up to {blas_threads} threads",
+        "per_layer": per_layer,
+    }
 
 
 def copy_calibration(mib: int) -> None:
@@ -75,54 +174,6 @@ def copy_calibration(mib: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
 
-
-def _source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def _traffic():
-    """HBM bytes per step from rocprofv3 counters, if taken on this kernel source."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256_16") != _source_hash():
-        return None
-    return t.get("bytes_per_launch")
-
-
-def cpu_baseline(layers_np, budget_s: float = 12.0):
-    """The CPU oracle (decode in float32, product in float64) on the same layers."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the interpreter's one thread
-        blas_threads = 1
-    done_bytes = 0
-    done_layers = 0
-    t0 = time.perf_counter()
-    while True:
-        for (layer, d, x, nbytes) in layers_np:
-            oracle.forward(x, d.codes, d.codebooks, d.scales)
-            done_bytes += nbytes
-            done_layers += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    _ = np
-    return {
-        "value": round(done_bytes / dt / 1e9, 4),
-        "unit": "GB/s",
-        "cores": int(blas_threads),
-        "kind": "oracle",
-        "sample": f"{done_layers} layer products of the seven Llama-2-7B 2x8 layers at batch 1 "
-                  f"(whole passes over the layer set, {dt:.1f} s); numpy decode is single-threaded, "
-                  f"the float64 product uses BLAS with up to {blas_threads} threads",
-    }
 
 
 def host_gemv_context(layers_np, budget_s: float = 2.0):
@@ -151,6 +202,7 @@ def host_gemv_context(layers_np, budget_s: float = 2.0):
     }
 
 
+
 def _capture(torch, fn):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -175,6 +227,7 @@ def _time_graph(torch, g, reps):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / reps
+
 
 
 def per_layer_tables(args):
@@ -299,6 +352,238 @@ def encode_tables(args):
     return rows
 
 
+
+def _layers_np(wname):
+    from additive_codebook_matmul_amd import workloads as WL
+    out = []
+    for layer in WL.WORKLOADS[wname].layers:
+        d = WL.make_layer(layer)
+        x = WL.make_x(layer, 1)
+        b = WL.workload_bytes(layer, 1)
+        out.append((layer, d, x, b["codes"] + b["x"] + b["y"]))
+    return out
+
+
+def _graph_ms(torch, g, min_ms=2.0):
+    """Mean milliseconds per replay of graph g over at least min_ms of replays."""
+    one = _time_graph(torch, g, 1)
+    reps = max(2, int(min_ms / max(one, 1e-3)) + 1)
+    return _time_graph(torch, g, reps)
+
+
+def scheme_step(torch, name, args, layers_np):
+    """The 32-block decode step of one scheme: timed steps, per-call and
+    per-layer times, the block as one call, and the dominant kernel's roofline."""
+    from additive_codebook_matmul_amd import AqlmLayer, gemv_batched
+    spec = SCHEME_SPECS[name]
+    dev = torch.device("cuda:0")
+    idx = {l.name: i for i, (l, _, _, _) in enumerate(layers_np)}
+    base = [(torch.from_numpy(d.codes.view("int16") if d.codes.dtype.name == "uint16" else d.codes)
+             .to(dev), torch.from_numpy(d.codebooks).to(dev), torch.from_numpy(d.scales).to(dev),
+             torch.from_numpy(x).to(dev)) for (_, d, x, _) in layers_np]
+    blocks = []
+    for _ in range(MODEL_BLOCKS):
+        row = {}
+        for (layer, _, _, _), (codes, books, scales, x) in zip(layers_np, base):
+            L = AqlmLayer(codes.clone(), books, scales.clone())
+            row[layer.name] = [L, x.clone(), torch.empty((1, L.out_features), dtype=torch.float16,
+                                                         device=dev)]
+        # q, k and v share one input, as do gate and up
+        for a, b in (("k", "q"), ("v", "q"), ("up", "gate")):
+            row[a][1] = row[b][1]
+        blocks.append(row)
+    torch.cuda.synchronize()
+    nbytes = {l.name: nb for (l, _, _, nb) in layers_np}
+    in2 = {l.name: 2 * l.in_features for (l, _, _, _) in layers_np}
+
+    def call_bytes(members):  # a shared input is read once per call
+        return sum(nbytes[m] for m in members) - (len(members) - 1) * in2[members[0]]
+
+    def issue(row, members):
+        if len(members) == 1:
+            L, xx, yy = row[members[0]]
+            L.gemv(xx, out=yy)
+        else:
+            gemv_batched([row[m][0] for m in members], [row[m][1] for m in members],
+                         [row[m][2] for m in members])
+
+    def step():
+        for row in blocks:
+            for _, members in CALLS:
+                issue(row, members)
+
+    step_graph = _capture(torch, step)
+    for _ in range(args.warmup):
+        step_graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step_graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    block_bytes = sum(call_bytes(m) for _, m in CALLS)
+    step_bytes = MODEL_BLOCKS * block_bytes
+
+    def over_blocks(fn):
+        g = _capture(torch, lambda: [fn(row) for row in blocks])
+        return 1e3 * _graph_ms(torch, g) / MODEL_BLOCKS
+
+    us_call = {cn: over_blocks(lambda row, m=m: issue(row, m)) for cn, m in CALLS}
+    us_layer = {n: over_blocks(lambda row, n=n: issue(row, (n,))) for n in idx}
+    one_call_us = over_blocks(lambda row: issue(row, tuple(idx)))
+    # the block's layers each in a call of its own: four fewer launches saved
+    dom_us = over_blocks(lambda row: [issue(row, m) for m in spec["dominant"]])
+    dom_launches = len(spec["dominant"])
+    dom_bytes = sum(call_bytes(m) for m in spec["dominant"])
+    avg_us = dom_us / dom_launches
+    achieved = (dom_bytes / dom_launches) / (avg_us * 1e-6) / 1e9
+    layer_gbps = {n: nbytes[n] / us_layer[n] / 1e3 for n in idx}
+    one_call_bytes = sum(nbytes.values())
+    res = {
+        "workload": spec["workload"],
+        "scheme": spec["scheme"],
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "ms_per_step": round(ms_per_step, 5),
+        "pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "bytes_per_step": step_bytes,
+        "block_step_us": round(1e3 * ms_per_step / MODEL_BLOCKS, 3),
+        "us_per_call": {k: round(v, 3) for k, v in us_call.items()},
+        "us_per_layer": {k: round(v, 3) for k, v in us_layer.items()},
+        "gbps_per_layer": {k: round(v, 1) for k, v in layer_gbps.items()},
+        "pct_of_peak_per_layer": {k: round(100 * v / HBM_PEAK_GBPS, 1) for k, v in layer_gbps.items()},
+        "block_as_one_call_us": round(one_call_us, 3),
+        "block_as_one_call_gbps": round(one_call_bytes / one_call_us / 1e3, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": spec["kernel"],
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": _traffic(spec),
+            "bytes_per_launch_avg": dom_bytes // dom_launches,
+            "avg_launch_us": round(avg_us, 3),
+            "launches_timed": dom_launches * MODEL_BLOCKS,
+        },
+    }
+    del blocks, step_graph
+    torch.cuda.empty_cache()
+    return res
+
+
+def _ceiling_lib():
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError(f"{CEILING_LIB} not built (python -m additive_codebook_matmul_amd.build)")
+    lib = ctypes.CDLL(CEILING_LIB)
+    lib.aqlm_ceiling_blocks.restype = ctypes.c_int
+    lib.aqlm_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    lib.aqlm_ceiling_gather.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def ceilings(torch, sizes):
+    """Pure-read ceiling at each byte count (cold: rotated buffers of >= 1 GiB
+    in all, one launch per buffer, inside a HIP graph; the fastest of 1..16
+    loads per thread), and the random 16-byte gather rate from a 1 MiB table
+    (the 1x16 codebook's size)."""
+    lib = _ceiling_lib()
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(max(lib.aqlm_ceiling_blocks(), (1 << 31) // 4096 + 1), dtype=torch.int32,
+                       device=dev)
+    stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    out = {}
+    for label, nb in sizes.items():
+        nb = (nb + 15) // 16 * 16
+        copies = max(2, min(256, -(-ROTATE_BYTES // nb)))
+        bufs = [torch.full((nb,), 1, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        best = None
+        for per_thread in (1, 2, 4, 8, 16):
+            def reads(bufs=bufs, nb=nb, pt=per_thread):
+                for b in bufs:
+                    if lib.aqlm_ceiling_read(b.data_ptr(), nb, pt, sink.data_ptr(), stream()) != 0:
+                        raise RuntimeError("aqlm_ceiling_read failed")
+            g = _capture(torch, reads)
+            us = 1e3 * _graph_ms(torch, g) / copies
+            if best is None or us < best[0]:
+                best = (us, per_thread)
+            del g
+        us, pt = best
+        out[label] = {"bytes": nb, "us": round(us, 3), "gbps": round(nb / us / 1e3, 1),
+                      "pct_hbm_peak": round(100 * nb / us / 1e3 / HBM_PEAK_GBPS, 1),
+                      "loads_per_thread": pt}
+        del bufs
+        torch.cuda.empty_cache()
+    table = torch.full((1 << 20,), 1, dtype=torch.uint8, device=dev)
+    per_lane = 256
+    lanes = lib.aqlm_ceiling_blocks() * 256
+
+    def gathers():
+        if lib.aqlm_ceiling_gather(table.data_ptr(), 16, per_lane, sink.data_ptr(), stream()) != 0:
+            raise RuntimeError("aqlm_ceiling_gather failed")
+    g = _capture(torch, gathers)
+    us = 1e3 * _graph_ms(torch, g)
+    rate = lanes * per_lane / (us * 1e-6)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    return {
+        "read": out,
+        "kernel": "aqlm_ceiling_read: 16-byte non-temporal loads, each byte once, a block of "
+                  "256 threads per 4096 * loads_per_thread bytes",
+        "gather_1mib": {"gathers_per_s": round(rate / 1e9, 2), "unit_rate": "G per s",
+                        "per_clk_per_cu": round(rate / (cus * CLOCK_GHZ * 1e9), 3),
+                        "code_gbps_at_one_gather_per_2_byte_code": round(2 * rate / 1e9, 1),
+                        "kernel": "aqlm_ceiling_gather: random 16-byte loads from a 1 MiB table"},
+    }
+
+
+def dense_fp16(torch, layers_np):
+    """torch.nn.functional.linear in float16 at the same seven shapes, batch 1,
+    on weights 8x the size of the 2-bit codes (rotated copies, >= 1 GiB)."""
+    import torch.nn.functional as F
+    dev = torch.device("cuda:0")
+    wbytes = sum(2 * l.out_features * l.in_features for (l, _, _, _) in layers_np)
+    copies = max(2, -(-ROTATE_BYTES // wbytes))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    ws = [[(torch.randn((l.out_features, l.in_features), generator=gen, device=dev) * 0.02)
+           .to(torch.float16) for (l, _, _, _) in layers_np] for _ in range(copies)]
+    xs = [torch.from_numpy(x).to(dev) for (_, _, x, _) in layers_np]
+
+    def blockstep():
+        for c in range(copies):
+            for w, x in zip(ws[c], xs):
+                F.linear(x, w)
+    g = None
+    try:
+        g = _capture(torch, blockstep)
+        us = 1e3 * _graph_ms(torch, g) / copies
+        how = "HIP graph"
+    except Exception as e:  # a BLAS path that cannot be captured: time it eagerly
+        torch.cuda.synchronize()
+        blockstep()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(5):
+            blockstep()
+        t1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * t0.elapsed_time(t1) / (5 * copies)
+        how = f"eager launches (graph capture failed: {type(e).__name__})"
+    xy = sum(2 * (l.in_features + l.out_features) for (l, _, _, _) in layers_np)
+    res = {"block_us": round(us, 3), "gbps": round((wbytes + xy) / us / 1e3, 1),
+           "pct_hbm_peak": round(100 * (wbytes + xy) / us / 1e3 / HBM_PEAK_GBPS, 1),
+           "weight_bytes_per_block": wbytes, "issue": how,
+           "op": "torch.nn.functional.linear, float16 weights [out, in], one activation row"}
+    del ws, g
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = _parse()
     if args.copy_calibration:
@@ -314,174 +599,35 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
+        sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from additive_codebook_matmul_amd import AqlmLayer, gemv_batched, load_library
-    from additive_codebook_matmul_amd import workloads as WL
+    from additive_codebook_matmul_amd import load_library
 
     load_library()
-    dev = torch.device("cuda:0")
-    wl = WL.WORKLOADS[WORKLOAD]
-
-    layers_np = []
-    for layer in wl.layers:
-        d = WL.make_layer(layer)
-        x = WL.make_x(layer, 1)
-        b = WL.workload_bytes(layer, 1)
-        layers_np.append((layer, d, x, b["codes"] + b["x"] + b["y"]))
-    code_bytes = sum(d.codes.nbytes for (_, d, _, _) in layers_np)
-    copies = max(2, -(-ROTATE_BYTES // code_bytes))
-
-    # device copies: copy c of layer l
-    base = []
-    for (layer, d, x, _) in layers_np:
-        base.append((torch.from_numpy(d.codes).to(dev), torch.from_numpy(d.codebooks).to(dev),
-                     torch.from_numpy(d.scales).to(dev), torch.from_numpy(x).to(dev)))
-    names = [l.name for (l, _, _, _) in layers_np]
-    idx = {n: i for i, n in enumerate(names)}
-    rot = []
-    for c in range(copies):
-        row = []
-        for (codes, books, scales, x) in base:
-            L = AqlmLayer(codes.clone(), books, scales.clone())
-            yy = torch.empty((1, L.out_features), dtype=torch.float16, device=dev)
-            row.append((L, x.clone(), yy))
-        # q, k, v share one input, as do gate and up
-        row[idx["k"]] = (row[idx["k"]][0], row[idx["q"]][1], row[idx["k"]][2])
-        row[idx["v"]] = (row[idx["v"]][0], row[idx["q"]][1], row[idx["v"]][2])
-        row[idx["up"]] = (row[idx["up"]][0], row[idx["gate"]][1], row[idx["up"]][2])
-        rot.append(row)
-    torch.cuda.synchronize()
-
-    calls = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
-    call_bytes = {cn: sum(layers_np[idx[n]][3] for n in members) for cn, members in calls}
-    for cn, members in calls:  # shared inputs are read once per call
-        if len(members) > 1:
-            call_bytes[cn] -= (len(members) - 1) * 2 * layers_np[idx[members[0]]][0].in_features
-
-    def issue(i, cn, members):
-        row = rot[i % copies]
-        if len(members) == 1:
-            L, xx, yy = row[idx[members[0]]]
-            L.gemv(xx, out=yy)
-        else:
-            items = [row[idx[m]] for m in members]
-            gemv_batched([it[0] for it in items], [it[1] for it in items],
-                         [it[2] for it in items])
-
-    def step(i):
-        for cn, members in calls:
-            issue(i, cn, members)
-
-    def capture(fn):
-        """A HIP graph of fn's launches (outputs are preallocated: nothing allocates)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        torch.cuda.synchronize()
-        return g
-
-    def time_graph(g, reps):
-        """Mean milliseconds per replay, HIP events on the replay stream."""
-        g.replay()
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / reps
-
-    # one graph holds one step on each rotated copy; a replay is `copies` steps
-    step_graph = capture(lambda: [step(i) for i in range(copies)])
-    for _ in range(max(1, args.warmup // copies)):
-        step_graph.replay()
-    reps = max(1, -(-args.steps // copies))
-    torch.cuda.synchronize()
-    ms_per_step = time_graph(step_graph, reps) / copies
-    steps_timed = reps * copies
-
-    # eager issue of the same step (host launch overhead included), for context
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    eager_ms_per_step = t0.elapsed_time(t1) / args.steps
-
-    # per call and per layer: graphs of back-to-back launches over the copies
-    call_us = {}
-    for cn, members in calls:
-        g = capture(lambda cn=cn, members=members: [issue(i, cn, members) for i in range(copies)])
-        call_us[cn] = 1e3 * time_graph(g, max(1, args.layer_iters // copies)) / copies
-    us_layer, gbps_layer = {}, {}
-    for li, (layer, _, _, nbytes) in enumerate(layers_np):
-        def one_layer(li=li):
-            for i in range(copies):
-                L, xx, yy = rot[i][li]
-                L.gemv(xx, out=yy)
-        g = capture(one_layer)
-        us = 1e3 * time_graph(g, max(1, args.layer_iters // copies)) / copies
-        us_layer[layer.name] = round(us, 3)
-        gbps_layer[layer.name] = round(nbytes / us / 1e3, 1)
-
-    # the whole block as one batched call (independent inputs)
-    def one_call_all():
-        for i in range(copies):
-            row = rot[i]
-            gemv_batched([r[0] for r in row], [r[1] for r in row], [r[2] for r in row])
-    g = capture(one_call_all)
-    one_call_us = 1e3 * time_graph(g, max(1, args.layer_iters // copies)) / copies
-
-    # dominant kernel: the grouped GEMV of the q,k,v and gate,up calls, launched
-    # back to back (one launch per call) inside the timed graph
-    def dominant():
-        for i in range(copies):
-            issue(i, "qkv", ["q", "k", "v"])
-            issue(i, "gate_up", ["gate", "up"])
-    g = capture(dominant)
-    dom_ms = time_graph(g, max(1, args.layer_iters // copies))
-    dom_launches = 2 * copies
-
-    step_bytes = sum(call_bytes.values())
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dom_bytes = call_bytes["qkv"] + call_bytes["gate_up"]
-    dom_avg_us = 1e3 * dom_ms / dom_launches
-    achieved = (dom_bytes / 2) / (dom_avg_us * 1e-6) / 1e9
-    traffic = _traffic()
-    roofline = {
-        "bound": "hbm",
-        "kernel": GEMV_KERNEL,
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": traffic,
-        "bytes_per_launch_avg": dom_bytes // 2,
-        "avg_launch_us": round(dom_avg_us, 3),
-    }
-
+    names = [s for s in args.schemes.split(",") if s]
+    if not names or names[0] != "2x8" or any(n not in SCHEME_SPECS for n in names):
+        print("--schemes must start with 2x8 (the reported value)", file=sys.stderr)
+        sys.exit(2)
+    layers_by_scheme = {n: _layers_np(SCHEME_SPECS[n]["workload"]) for n in names}
+    schemes = {}
+    for n in names:
+        print(f"[bench] scheme {n}: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr,
+              flush=True)
+        schemes[n] = scheme_step(torch, n, args, layers_by_scheme[n])
+    head = schemes["2x8"]
+    layers_np = layers_by_scheme["2x8"]
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["value"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps_timed,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -489,26 +635,41 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD,
-            "scheme": "2x8 (M=2, B=8, g=8)",
+            "scheme": head["scheme"],
             "batch": 1,
+            "blocks_per_step": MODEL_BLOCKS,
             "layers": {l.name: [l.out_features, l.in_features] for (l, _, _, _) in layers_np},
-            "bytes_per_step": step_bytes,
-            "rotated_copies": copies,
-            "step_calls": {cn: members for cn, members in calls},
-            "us_per_call": {k: round(v, 3) for k, v in call_us.items()},
-            "us_per_layer": us_layer,
-            "gbps_per_layer": gbps_layer,
-            "pct_of_peak_per_layer": {k: round(100 * v / HBM_PEAK_GBPS, 1)
-                                      for k, v in gbps_layer.items()},
+            "bytes_per_step": head["bytes_per_step"],
+            "step": "one token through the linear layers of 32 Llama-2-7B blocks (224 launches' "
+                    "worth of layers, 128 calls), each block's codes in buffers of their own",
+            "step_calls": {cn: list(m) for cn, m in CALLS},
+            "block_step_us": head["block_step_us"],
+            "us_per_call": head["us_per_call"],
+            "us_per_layer": head["us_per_layer"],
+            "gbps_per_layer": head["gbps_per_layer"],
+            "pct_of_peak_per_layer": head["pct_of_peak_per_layer"],
+            "block_as_one_call_us": head["block_as_one_call_us"],
+            "block_as_one_call_gbps": head["block_as_one_call_gbps"],
             "accumulate": "fp32",
-            "issue": "HIP graph of the step's launches (eager issue in eager_ms_per_step)",
-            "eager_ms_per_step": round(eager_ms_per_step, 5),
-            "block_as_one_call_us": round(one_call_us, 3),
-            "block_as_one_call_gbps": round(sum(nb for (_, _, _, nb) in layers_np) / one_call_us / 1e3, 1),
+            "issue": "HIP graph of the step's launches, replayed once per timed step",
         },
-        "roofline": roofline,
+        "roofline": head["roofline"],
+        "schemes": schemes,
+        "rooflines": {n: s["roofline"] for n, s in schemes.items()},
     }
+    if not args.no_context:
+        print("[bench] ceilings and dense fp16", file=sys.stderr, flush=True)
+        sizes = {"layer_4096x4096": layers_np[0][3], "layer_11008x4096": layers_np[4][3],
+                 "call_qkv": 3 * layers_np[0][3], "call_gate_up": 2 * layers_np[4][3],
+                 "block": sum(nb for (_, _, _, nb) in layers_np),
+                 "step_32_blocks": MODEL_BLOCKS * sum(nb for (_, _, _, nb) in layers_np)}
+        result["ceiling"] = ceilings(torch, sizes)
+        blk = result["ceiling"]["read"]["block"]["us"]
+        for n, s in schemes.items():
+            s["block_as_one_call_pct_of_read_ceiling"] = round(100 * blk / s["block_as_one_call_us"], 1)
+        result["dense_fp16"] = dense_fp16(torch, layers_np)
     if not args.no_cpu_baseline:
+        print("[bench] cpu oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(layers_np)
     if not args.no_host_gemv:
         result["host_gemv"] = host_gemv_context(layers_np)
