@@ -21,10 +21,10 @@ AQLM_OK = 0
 STATUS_NAMES = {0: "AQLM_OK", 1: "AQLM_ERR_NULL", 2: "AQLM_ERR_SHAPE", 3: "AQLM_ERR_SCHEME",
                 4: "AQLM_ERR_ALIGN", 5: "AQLM_ERR_BATCH", 6: "AQLM_ERR_HIP",
                 7: "AQLM_ERR_WORKSPACE", 8: "AQLM_ERR_SCRATCH"}
-EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemv_batched", "aqlm_gemm",
-                    "aqlm_gemm_workspace_size", "aqlm_gemm_ws", "aqlm_gemm_noalloc",
-                    "aqlm_status_string", "aqlm_abi_version")
-ABI_VERSION = 4
+EXPORTED_SYMBOLS = ("aqlm_dequant", "aqlm_gemv", "aqlm_gemv_batched", "aqlm_gemv_workspace_size",
+                    "aqlm_gemv_ws", "aqlm_gemm", "aqlm_gemm_workspace_size", "aqlm_gemm_ws",
+                    "aqlm_gemm_noalloc", "aqlm_status_string", "aqlm_abi_version")
+ABI_VERSION = 5
 # bytes of the library's static scratch array (AQLM_STATIC_SCRATCH_BYTES)
 STATIC_SCRATCH_BYTES = 64 << 20
 AQLM_CODES_PACKED = 1
@@ -85,6 +85,13 @@ def load_library() -> ctypes.CDLL:
                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32,
                                       ctypes.c_int64, ctypes.c_void_p]
     lib.aqlm_gemv_batched.restype = ctypes.c_int
+    lib.aqlm_gemv_workspace_size.argtypes = [lp, ctypes.c_int32, ctypes.c_int64,
+                                             ctypes.POINTER(ctypes.c_int64)]
+    lib.aqlm_gemv_workspace_size.restype = ctypes.c_int
+    lib.aqlm_gemv_ws.argtypes = [lp, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                 ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_void_p]
+    lib.aqlm_gemv_ws.restype = ctypes.c_int
     lib.aqlm_status_string.argtypes = [ctypes.c_int]
     lib.aqlm_status_string.restype = ctypes.c_char_p
     lib.aqlm_abi_version.argtypes = []
@@ -204,9 +211,18 @@ class AqlmLayer:
                                          out.data_ptr(), _stream_handle(self.device)))
         return out
 
-    def gemv(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """y = x . W^T for 1..8 activation rows (codebook-lookup path)."""
-        return self._product("aqlm_gemv", x, out)
+    def gemv(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+             workspace: bool = True) -> torch.Tensor:
+        """y = x . W^T for 1..8 activation rows (codebook-lookup path).
+
+        With workspace=True (the default) the call goes through aqlm_gemv_ws
+        with a workspace taken from torch's allocator on the current stream
+        (used by the codebook-sliced 1x16 kernel at one row); workspace=False
+        calls aqlm_gemv, which needs none.
+        """
+        if not workspace:
+            return self._product("aqlm_gemv", x, out)
+        return gemv_batched([self], [x], None if out is None else [out])[0]
 
     def workspace_bytes(self, batch: int) -> int:
         """Device workspace aqlm_gemm_ws needs for this batch (0: none)."""
@@ -254,12 +270,15 @@ class AqlmLayer:
         return self.gemv(x) if x.shape[0] <= 8 else self.gemm(x)
 
 
-def gemv_batched(layers, xs, outs=None):
-    """y_i = x_i . W_i^T for several layers in one call (aqlm_gemv_batched).
+def gemv_batched(layers, xs, outs=None, workspace: bool = True):
+    """y_i = x_i . W_i^T for several layers in one call.
 
     layers: sequence of AqlmLayer; xs: sequence of [batch, in_i] float16 tensors
     (one per layer, all with the same batch, may repeat); outs: optional
-    preallocated [batch, out_i] tensors. Returns the list of outputs.
+    preallocated [batch, out_i] tensors. Returns the list of outputs. With
+    workspace=True (the default) the call is aqlm_gemv_ws with a workspace
+    from torch's allocator on the current stream; workspace=False calls
+    aqlm_gemv_batched.
     """
     lib = load_library()
     n = len(layers)
@@ -286,8 +305,25 @@ def gemv_batched(layers, xs, outs=None):
     xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
     yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     with torch.cuda.device(device):
-        _check(lib.aqlm_gemv_batched(structs, xp, yp, n, batch, _stream_handle(device)))
+        if not workspace:
+            _check(lib.aqlm_gemv_batched(structs, xp, yp, n, batch, _stream_handle(device)))
+            return ys
+        need = ctypes.c_int64(0)
+        _check(lib.aqlm_gemv_workspace_size(structs, n, batch, ctypes.byref(need)))
+        ws = torch.empty(need.value, dtype=torch.uint8, device=device) if need.value else None
+        _check(lib.aqlm_gemv_ws(structs, xp, yp, n, batch,
+                                ws.data_ptr() if ws is not None else None, need.value,
+                                _stream_handle(device)))
     return ys
+
+
+def gemv_workspace_bytes(layers, batch: int) -> int:
+    """Device workspace aqlm_gemv_ws needs for these layers at this batch (0: none)."""
+    n = len(layers)
+    structs = (AqlmLayerStruct * n)(*[L._struct for L in layers])
+    need = ctypes.c_int64(0)
+    _check(load_library().aqlm_gemv_workspace_size(structs, n, int(batch), ctypes.byref(need)))
+    return need.value
 
 
 def raw_call(fn_name: str, struct: AqlmLayerStruct, *args) -> int:

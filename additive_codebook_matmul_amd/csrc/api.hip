@@ -55,6 +55,27 @@ int check_layer(const aqlm_layer *layer, aqlm::LayerDesc *d) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? AQLM_OK : AQLM_ERR_HIP; }
 
+// Validation shared by the grouped GEMV entry points: fills d; checks x and
+// y unless check_io is false.
+int check_layers(const aqlm_layer *layers, const uint16_t *const *x, uint16_t *const *y,
+                 int32_t num_layers, int64_t batch, std::vector<aqlm::LayerDesc> *d,
+                 bool check_io) {
+  if (num_layers < 0 || num_layers > 4096) return AQLM_ERR_SHAPE;
+  if (batch < 0 || batch > 8) return AQLM_ERR_BATCH;
+  if (num_layers == 0 || batch == 0) return AQLM_OK;
+  if (!layers) return AQLM_ERR_NULL;
+  if (check_io && (!x || !y)) return AQLM_ERR_NULL;
+  d->resize(num_layers);
+  for (int i = 0; i < num_layers; ++i) {
+    const int st = check_layer(&layers[i], &(*d)[i]);
+    if (st != AQLM_OK) return st;
+    if (!check_io) continue;
+    if (!x[i] || !y[i]) return AQLM_ERR_NULL;
+    if (!aligned16(x[i]) || !aligned16(y[i])) return AQLM_ERR_ALIGN;
+  }
+  return AQLM_OK;
+}
+
 }  // namespace
 
 // Scratch memory of aqlm_gemm_noalloc: a static device array, one copy per GPU
@@ -133,19 +154,39 @@ int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_
 
 int aqlm_gemv_batched(const aqlm_layer *layers, const uint16_t *const *x, uint16_t *const *y,
                       int32_t num_layers, int64_t batch, void *stream) {
-  if (num_layers < 0 || num_layers > 4096) return AQLM_ERR_SHAPE;
-  if (batch < 0 || batch > 8) return AQLM_ERR_BATCH;
-  if (num_layers == 0 || batch == 0) return AQLM_OK;
-  if (!layers || !x || !y) return AQLM_ERR_NULL;
-  std::vector<aqlm::LayerDesc> d(num_layers);
-  for (int i = 0; i < num_layers; ++i) {
-    const int st = check_layer(&layers[i], &d[i]);
-    if (st != AQLM_OK) return st;
-    if (!x[i] || !y[i]) return AQLM_ERR_NULL;
-    if (!aligned16(x[i]) || !aligned16(y[i])) return AQLM_ERR_ALIGN;
-  }
+  std::vector<aqlm::LayerDesc> d;
+  const int st = check_layers(layers, x, y, num_layers, batch, &d, true);
+  if (st != AQLM_OK || num_layers == 0 || batch == 0) return st;
   return from_hip(aqlm::launch_gemv_batched(d.data(), x, y, num_layers, (int)batch,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int aqlm_gemv_workspace_size(const aqlm_layer *layers, int32_t num_layers, int64_t batch,
+                             int64_t *bytes) {
+  if (!bytes) return AQLM_ERR_NULL;
+  *bytes = 0;
+  std::vector<aqlm::LayerDesc> d;
+  const int st = check_layers(layers, nullptr, nullptr, num_layers, batch, &d, false);
+  if (st != AQLM_OK) return st;
+  if (num_layers == 0 || batch == 0) return AQLM_OK;
+  *bytes = aqlm::gemv_ws_bytes(d.data(), num_layers, (int)batch);
+  return AQLM_OK;
+}
+
+int aqlm_gemv_ws(const aqlm_layer *layers, const uint16_t *const *x, uint16_t *const *y,
+                 int32_t num_layers, int64_t batch, void *workspace, int64_t workspace_bytes,
+                 void *stream) {
+  std::vector<aqlm::LayerDesc> d;
+  const int st = check_layers(layers, x, y, num_layers, batch, &d, true);
+  if (st != AQLM_OK) return st;
+  if (num_layers == 0 || batch == 0) return AQLM_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t need = aqlm::gemv_ws_bytes(d.data(), num_layers, (int)batch);
+  if (need == 0) return from_hip(aqlm::launch_gemv_batched(d.data(), x, y, num_layers, (int)batch, s));
+  if (!workspace) return AQLM_ERR_NULL;
+  if (!aligned16(workspace)) return AQLM_ERR_ALIGN;
+  if (workspace_bytes < need) return AQLM_ERR_WORKSPACE;
+  return from_hip(aqlm::launch_gemv_batched_ws(d.data(), x, y, num_layers, (int)batch, workspace, s));
 }
 
 namespace {

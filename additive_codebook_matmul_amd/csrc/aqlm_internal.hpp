@@ -69,5 +69,19 @@ hipError_t launch_gemv_2x8_mfma_batched(const LayerDesc *Ls, const uint16_t *con
                                         hipStream_t stream);
 hipError_t launch_gemv_batched(const LayerDesc *Ls, const uint16_t *const *xs,
                                uint16_t *const *ys, int n, int batch, hipStream_t stream);
+// Codebook-sliced 1x16 GEMV for one activation row (gemv_slice.hip): whether
+// it serves a layer, the workspace it needs there (float32 member sums), and
+// a launch of up to 16 such layers (plus the launch that adds the sums).
+bool gemv_slice_fits(const LayerDesc &L, int batch);
+int64_t gemv_slice_ws_bytes(const LayerDesc &L);
+hipError_t launch_gemv_slice(const LayerDesc *const *Ls, const uint16_t *const *xs,
+                             uint16_t *const *ys, float *const *parts, int n, hipStream_t stream);
+// Workspace form of the grouped GEMV: the layers gemv_slice_fits accepts run
+// the sliced kernel on workspace parts laid out in layer order; the others
+// run as in launch_gemv_batched.
+int64_t gemv_ws_bytes(const LayerDesc *Ls, int n, int batch);
+hipError_t launch_gemv_batched_ws(const LayerDesc *Ls, const uint16_t *const *xs,
+                                  uint16_t *const *ys, int n, int batch, void *ws,
+                                  hipStream_t stream);
 
 }  // namespace aqlm

@@ -625,4 +625,68 @@ hipError_t launch_gemv_batched(const LayerDesc *Ls, const uint16_t *const *xs,
   return hipSuccess;
 }
 
+// The codebook-sliced kernel pays a fixed cost per call (staging each
+// member's 128 KiB of codewords, a second launch for the sums) and then runs
+// about 1.5x faster per code than the gather kernel: it wins from about 2^22
+// codes (8 MiB) in the call's eligible layers (a 4096x4096 layer alone is
+// 2^21). Below that the call runs the gather kernel.
+constexpr int64_t kSliceMinCallCodes = int64_t(1) << 22;
+
+bool call_uses_slices(const LayerDesc *Ls, int n, int batch) {
+  int64_t codes = 0;
+  for (int i = 0; i < n; ++i)
+    if (gemv_slice_fits(Ls[i], batch)) codes += Ls[i].out * Ls[i].groups;
+  return codes >= kSliceMinCallCodes;
+}
+
+int64_t gemv_ws_bytes(const LayerDesc *Ls, int n, int batch) {
+  if (!call_uses_slices(Ls, n, batch)) return 0;
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i)
+    if (gemv_slice_fits(Ls[i], batch)) total += gemv_slice_ws_bytes(Ls[i]);
+  return total;
+}
+
+hipError_t launch_gemv_batched_ws(const LayerDesc *Ls, const uint16_t *const *xs,
+                                  uint16_t *const *ys, int n, int batch, void *ws,
+                                  hipStream_t stream) {
+  if (!call_uses_slices(Ls, n, batch)) return launch_gemv_batched(Ls, xs, ys, n, batch, stream);
+  // sliced layers: up to 16 per launch, each with its part of the workspace
+  constexpr int kGroup = 16;
+  const LayerDesc *sel[kGroup];
+  const uint16_t *sx[kGroup];
+  uint16_t *sy[kGroup];
+  float *sp[kGroup];
+  int m = 0;
+  uint8_t *w = static_cast<uint8_t *>(ws);
+  std::vector<LayerDesc> rest_l;
+  std::vector<const uint16_t *> rest_x;
+  std::vector<uint16_t *> rest_y;
+  for (int i = 0; i < n; ++i) {
+    if (!gemv_slice_fits(Ls[i], batch)) {
+      rest_l.push_back(Ls[i]);
+      rest_x.push_back(xs[i]);
+      rest_y.push_back(ys[i]);
+      continue;
+    }
+    sel[m] = &Ls[i];
+    sx[m] = xs[i];
+    sy[m] = ys[i];
+    sp[m] = reinterpret_cast<float *>(w);
+    w += gemv_slice_ws_bytes(Ls[i]);
+    if (++m == kGroup) {
+      const hipError_t e = launch_gemv_slice(sel, sx, sy, sp, m, stream);
+      if (e != hipSuccess) return e;
+      m = 0;
+    }
+  }
+  if (m > 0) {
+    const hipError_t e = launch_gemv_slice(sel, sx, sy, sp, m, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (rest_l.empty()) return hipSuccess;
+  return launch_gemv_batched(rest_l.data(), rest_x.data(), rest_y.data(), (int)rest_l.size(),
+                             batch, stream);
+}
+
 }  // namespace aqlm

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define AQLM_ABI_VERSION 4
+#define AQLM_ABI_VERSION 5
 
 /* aqlm_layer.flags: codes are bit-packed (see the format above). */
 #define AQLM_CODES_PACKED 1
@@ -183,6 +183,51 @@ AQLM_API int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, in
  */
 AQLM_API int aqlm_gemm_ws(const aqlm_layer *layer, const uint16_t *x, int64_t batch, uint16_t *y,
                           void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * aqlm_gemv_workspace_size: bytes of device workspace that aqlm_gemv_ws needs
+ * for these num_layers layers (a HOST array) at this batch, written to
+ * *bytes (0 when the call needs none and runs exactly as aqlm_gemv_batched).
+ * It depends only on the layers' shapes and schemes and on batch: 32 * out
+ * bytes, rounded up to 256, for each 1x16 layer (g = 8) that the
+ * codebook-sliced kernel serves at one activation row (in / 8 a multiple of
+ * 8, at most 4096 groups per row, at least 2^19 codes), provided those layers
+ * hold at least 2^22 codes together (below that the call runs the gather
+ * kernel of aqlm_gemv_batched and needs nothing). Validation and status codes
+ * as for aqlm_gemv_batched; *bytes is 0 on error.
+ */
+AQLM_API int aqlm_gemv_workspace_size(const aqlm_layer *layers, int32_t num_layers, int64_t batch,
+                                      int64_t *bytes);
+
+/*
+ * aqlm_gemv_ws: aqlm_gemv_batched with a caller-owned device workspace (one
+ * layer: num_layers = 1). Where aqlm_gemv_workspace_size counts a layer, that
+ * layer runs the codebook-sliced 1x16 kernel: its 1 MiB codebook is split
+ * over the LDS of a team of eight workgroups (four 16384-codeword slices by
+ * the top two code bits, times two halves of each codeword), every member
+ * reads all of the team's codes and looks up those of its slice, and a
+ * second launch adds the eight members' float32 partial sums in a fixed
+ * order, scales and rounds ("AQLM (additive / multi-codebook quantization)",
+ * field "Kernels": lookup without per-element dequantization). Such layers
+ * with the same row length (in 1 KiB code chunks) share one launch. Every
+ * other layer runs exactly as in aqlm_gemv_batched (same kernels, same bits).
+ *   workspace        device pointer, 16-byte aligned, at least
+ *                    aqlm_gemv_workspace_size bytes (NULL allowed when that
+ *                    size is 0); overwritten by the call; must not overlap x
+ *                    or y
+ *   workspace_bytes  its size in bytes
+ * Results are deterministic (the same call gives the same bits) and meet the
+ * product tolerance. For the layers the sliced kernel serves they differ in
+ * the last bits from aqlm_gemv, which sums in another order; since the
+ * kernel is chosen per call (by the codes of its eligible layers), a 1x16
+ * layer may give different last bits alone and in a larger call. Calls on
+ * different streams need different workspaces. Returns AQLM_ERR_WORKSPACE if workspace_bytes is too small,
+ * AQLM_ERR_NULL if the workspace is needed and NULL, AQLM_ERR_ALIGN if it is
+ * misaligned; otherwise as aqlm_gemv_batched.
+ */
+AQLM_API int aqlm_gemv_ws(const aqlm_layer *layers, const uint16_t *const *x, uint16_t *const *y,
+                          int32_t num_layers, int64_t batch, void *workspace,
+                          int64_t workspace_bytes, void *stream);
 
 /*
  * aqlm_gemm_noalloc: aqlm_gemm_ws with no workspace argument and no device

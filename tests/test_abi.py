@@ -234,6 +234,62 @@ def test_batched_validation():
     assert f(good, xs, ys, n, 0, None) == 0
 
 
+def _gemv_ws_size(layers, batch):
+    n = len(layers)
+    arr = (_lib.AqlmLayerStruct * n)(*layers) if n else None
+    v = ctypes.c_int64(-1)
+    st = _lib.load_library().aqlm_gemv_workspace_size(arr, n, batch, ctypes.byref(v))
+    return st, v.value
+
+
+def test_gemv_workspace_size():
+    """The codebook-sliced 1x16 kernel's workspace: 8 float32 sums per output
+    row (rounded to 256 bytes) for 1x16 g8 layers at one activation row with
+    in/8 a multiple of 8, at most 4096 groups and at least 2^19 codes, when
+    those layers hold at least 2^22 codes together; none for anything else."""
+    big = _layer(1, 16, 8, out=11008, n_in=4096)                         # 5.6 M codes
+    assert _gemv_ws_size([big], 1) == (0, 8 * 11008 * 4)
+    assert _gemv_ws_size([big], 2) == (0, 0)                              # batch 1 only
+    q = _layer(1, 16, 8, out=4096, n_in=4096)                             # 2^21 codes
+    assert _gemv_ws_size([q], 1) == (0, 0)                                # alone: too few
+    assert _gemv_ws_size([q, q], 1) == (0, 2 * 8 * 4096 * 4)              # 2^22 together
+    assert _gemv_ws_size([q, q, q], 1) == (0, 3 * 8 * 4096 * 4)
+    assert _gemv_ws_size([_layer(2, 8, 8, out=11008, n_in=4096)], 1) == (0, 0)   # 2x8
+    assert _gemv_ws_size([_layer(1, 16, 16, out=11008, n_in=8192)], 1) == (0, 0)  # g16
+    small = _layer(1, 16, 8, out=100, n_in=4096)                          # below 2^19: never
+    assert _gemv_ws_size([small, big], 1) == (0, 8 * 11008 * 4)
+    assert _gemv_ws_size([_layer(1, 16, 8, out=8200, n_in=4096)], 1) == (0, (8 * 8200 * 4 + 255) // 256 * 256)
+    assert _gemv_ws_size([_layer(1, 16, 8, out=16384, n_in=36 * 8 * 8 + 8)], 1) == (0, 0)  # in/8 % 8
+    assert _gemv_ws_size([_layer(1, 16, 8, out=1200, n_in=28672)], 1)[1] > 0  # 7 chunks per row
+    assert _gemv_ws_size([_layer(1, 16, 8, out=1200, n_in=40960)], 1) == (0, 0)  # > 4096 groups
+    three = [big, _layer(2, 8, 8, out=4096, n_in=4096), q]
+    assert _gemv_ws_size(three, 1) == (0, 8 * 11008 * 4 + 8 * 4096 * 4)
+    assert _gemv_ws_size(three, 0) == (0, 0)
+    assert _gemv_ws_size([], 1) == (0, 0)
+    assert _gemv_ws_size([_layer(M=9)], 1) == (3, 0)
+    assert _gemv_ws_size([big], 9) == (5, 0)
+    assert _lib.load_library().aqlm_gemv_workspace_size(None, 1, 1, None) == 1
+
+
+def test_gemv_ws_validation():
+    """Errors of aqlm_gemv_ws that stop the call before any launch."""
+    f = _lib.load_library().aqlm_gemv_ws
+    one = (_lib.AqlmLayerStruct * 1)(_layer(1, 16, 8, out=11008, n_in=4096))
+    xs = (ctypes.c_void_p * 1)(FAKE)
+    ys = (ctypes.c_void_p * 1)(FAKE + 0x1000)
+    need = 8 * 11008 * 4
+    assert f(one, xs, ys, 1, 1, None, need, None) == 1
+    assert f(one, xs, ys, 1, 1, MISALIGNED, need, None) == 4
+    assert f(one, xs, ys, 1, 1, FAKE, need - 1, None) == 7
+    assert f(one, xs, ys, 1, 9, FAKE, need, None) == 5
+    assert f(one, None, ys, 1, 1, FAKE, need, None) == 1
+    assert f(one, xs, ys, -1, 1, FAKE, need, None) == 2
+    bad_y = (ctypes.c_void_p * 1)(MISALIGNED)
+    assert f(one, xs, bad_y, 1, 1, FAKE, need, None) == 4
+    assert f(one, xs, ys, 1, 0, None, 0, None) == 0   # batch 0: no-op
+    assert f(one, xs, ys, 0, 1, None, 0, None) == 0   # no layers: no-op
+
+
 @pytest.mark.parametrize("M,B,g", [(1, 8, 8), (3, 8, 8), (8, 8, 16), (1, 12, 8), (2, 12, 16),
                                    (2, 16, 8), (8, 16, 16), (4, 9, 8), (5, 15, 16)])
 def test_general_schemes_accepted(M, B, g):

@@ -23,9 +23,9 @@ def _layers(wname):
 def test_batched_matches_single_launches_llama2_7b(batch):
     layers = _layers("llama2_7b_2x8")
     xs = [dev_x(WL.make_x(l, batch)) for (l, _, _) in layers]
-    ys = gemv_batched([L for (_, _, L) in layers], xs)
+    ys = gemv_batched([L for (_, _, L) in layers], xs, workspace=False)
     for (layer, d, L), x, y in zip(layers, xs, ys):
-        y1 = L.gemv(x)
+        y1 = L.gemv(x, workspace=False)
         assert np.array_equal(bits(y), bits(y1)), layer.name
     # and against the oracle on two of them
     for i in (0, 6):
@@ -33,6 +33,26 @@ def test_batched_matches_single_launches_llama2_7b(batch):
         xn = WL.make_x(layer, batch)
         y_ref, bound = oracle.forward(xn, d.codes, d.codebooks, d.scales)
         assert_product(ys[i], y_ref, bound, f"batched {layer.name}")
+
+
+def test_batched_1x16_llama2_7b_both_entry_points():
+    """The 1x16 layer set at one row: aqlm_gemv_batched equals aqlm_gemv bit
+    for bit (no workspace: the gather kernel); the workspace call (the q,k,v
+    and gate,up calls are large enough for the codebook-sliced kernel) meets
+    the oracle on every layer."""
+    layers = _layers("llama2_7b_1x16")
+    xs = [dev_x(WL.make_x(l, 1)) for (l, _, _) in layers]
+    Ls = [L for (_, _, L) in layers]
+    ys = gemv_batched(Ls, xs, workspace=False)
+    for (layer, d, L), x, y in zip(layers, xs, ys):
+        assert np.array_equal(bits(y), bits(L.gemv(x, workspace=False))), layer.name
+    for names in (("q", "k", "v"), ("gate", "up")):
+        idx = [i for i, (l, _, _) in enumerate(layers) if l.name in names]
+        yw = gemv_batched([Ls[i] for i in idx], [xs[i] for i in idx])
+        for i, y in zip(idx, yw):
+            layer, d, _ = layers[i]
+            y_ref, bound = oracle.forward(WL.make_x(layer, 1), d.codes, d.codebooks, d.scales)
+            assert_product(y, y_ref, bound, f"workspace call {layer.name}")
 
 
 def test_batched_shared_x_and_mixed_schemes():

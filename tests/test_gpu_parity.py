@@ -259,13 +259,33 @@ def test_gemv_rows_per_wavefront_same_bits(batch):
     row count (1024, 4096 and 12288 rows here); a row's sum, and so its bits,
     must not depend on that. The taller layers repeat the 1024-row codes."""
     c, b, sc, x = WL.small_case(1024, 1024, WL.S1x16, batch, seed=11)
-    y0 = dev_layer(c, b, sc).gemv(dev_x(x)).cpu().numpy()
+    y0 = dev_layer(c, b, sc).gemv(dev_x(x), workspace=False).cpu().numpy()
     y_ref, bound = oracle.forward(x, c, b, sc)
     assert_product(y0, y_ref, bound, f"1024 rows b{batch}")
     for k in (4, 12):
-        yk = dev_layer(np.tile(c, (k, 1, 1)), b, np.tile(sc, k)).gemv(dev_x(x)).cpu().numpy()
+        yk = dev_layer(np.tile(c, (k, 1, 1)), b, np.tile(sc, k)).gemv(
+            dev_x(x), workspace=False).cpu().numpy()
         for i in range(k):
             assert_bit_exact(yk[:, i * 1024:(i + 1) * 1024], y0, f"{1024 * k} rows, copy {i}")
+
+
+def test_sliced_gemv_rows_same_bits_wherever_they_sit():
+    """The codebook-sliced kernel (aqlm_gemv_ws, 1x16, one row) splits rows
+    over 32 teams by the layer's row count; a row's bits must not depend on
+    which team, wavefront or ring slot computes it. The taller layers repeat
+    the 8200-row codes (16400 and 16401 rows: a ragged last team)."""
+    c, b, sc, x = WL.small_case(8200, 4096, WL.S1x16, 1, seed=12)
+    L0 = dev_layer(c, b, sc)
+    assert _lib.gemv_workspace_bytes([L0], 1) > 0
+    y0 = L0.gemv(dev_x(x)).cpu().numpy()
+    y_ref, bound = oracle.forward(x, c, b, sc)
+    assert_product(y0, y_ref, bound, "8200 rows, sliced")
+    for k, extra in ((2, 0), (2, 1)):
+        ck = np.concatenate([np.tile(c, (k, 1, 1)), c[:extra]])
+        sk = np.concatenate([np.tile(sc, k), sc[:extra]])
+        yk = dev_layer(ck, b, sk).gemv(dev_x(x)).cpu().numpy()
+        for i in range(k):
+            assert_bit_exact(yk[:, i * 8200:(i + 1) * 8200], y0, f"{8200 * k + extra} rows, copy {i}")
 
 
 # the workload's batches plus batches of the workspace GEMM (1..16 rows: one
