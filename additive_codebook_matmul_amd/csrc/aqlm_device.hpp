@@ -10,6 +10,8 @@
 namespace aqlm {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
@@ -169,6 +171,10 @@ __device__ __forceinline__ uint32_t decode_word1(uint32_t a, float s) {
 // DPP row/bank controls (gfx9 family).
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppQuadBcast0 = 0x00;   // quad_perm [0,0,0,0]
+constexpr int kDppQuadBcast1 = 0x55;   // quad_perm [1,1,1,1]
+constexpr int kDppQuadBcast2 = 0xAA;   // quad_perm [2,2,2,2]
+constexpr int kDppQuadBcast3 = 0xFF;   // quad_perm [3,3,3,3]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowBcast15 = 0x142;
@@ -199,6 +205,16 @@ __device__ __forceinline__ float row_sum(float v) {
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   v += dpp<kDppQuadXor1>(v);
   v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  v += dpp<kDppRowBcast15, 0xA>(v);
+  v += dpp<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+// Sum over the 16 quads of a wavefront when every lane of a quad holds its
+// quad's value, in a fixed order; the total is valid in lane 63.
+__device__ __forceinline__ float quads_sum_to_lane63(float v) {
   v += dpp<kDppRowHalfMirror>(v);
   v += dpp<kDppRowMirror>(v);
   v += dpp<kDppRowBcast15, 0xA>(v);

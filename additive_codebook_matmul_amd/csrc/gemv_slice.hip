@@ -10,7 +10,8 @@
 // of the team's rows (coalesced 16-byte loads; the other seven members read
 // the same lines, mostly from L2), looks up only the codes of its slice (an
 // 8-byte LDS read; other codes read a zero entry) and takes the dot product of
-// that half-codeword with the matching four activations. A row's eight member
+// that half-codeword with the matching four activations on the matrix cores
+// (4x4x4 products, whose diagonals hold the lanes' own dot products). A row's eight member
 // sums go to the workspace, and a second launch adds them in member order,
 // applies the row scale and rounds to float16. Random 8-byte LDS reads cost
 // about a third of a clock per lane, against several clocks per L2 codeword
@@ -29,10 +30,10 @@
 //     512c + 8l .. 512c + 8l + 7 of chunk c, so every lane keeps the
 //     activations of its groups (its half of each) in registers for the whole
 //     kernel; the codes of the next D rows are in flight;
-//   * a code's slice test, entry index and address take three VALU
+//   * the slice test and entry indexes of a word of two codes take two VALU
 //     operations: t = w ^ (v << 14 | v << 30) clears the top two bits of each
-//     16-bit half of a slice-v code, so min(half(t), 16384) is the entry index
-//     of a hit and the zero entry 16384 of a miss.
+//     16-bit half of a slice-v code, so a packed 16-bit min(t, 16384) gives
+//     the entry index of a hit and the zero entry 16384 of a miss, per half.
 #include <atomic>
 
 #include "aqlm_device.hpp"
@@ -60,6 +61,24 @@ struct SliceArgs {
   SliceLayer layer[kSlMaxGroup];
   int n;
 };
+
+// LDS byte address of the entry whose index is the low (high) 16 bits of m:
+// index * 8 + base in one v_mad_u32_u16 (op_sel picks the high half).
+__device__ __forceinline__ uint32_t entry_addr_lo(uint32_t m, uint32_t base) {
+  uint32_t r;
+  asm("v_mad_u32_u16 %0, %1, 8, %2" : "=v"(r) : "v"(m), "s"(base));
+  return r;
+}
+__device__ __forceinline__ uint32_t entry_addr_hi(uint32_t m, uint32_t base) {
+  uint32_t r;
+  asm("v_mad_u32_u16 %0, %1, 8, %2 op_sel:[1,0,0,0]" : "=v"(r) : "v"(m), "s"(base));
+  return r;
+}
+__device__ __forceinline__ uint2 lds_load8(uint32_t addr) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = *reinterpret_cast<__attribute__((address_space(3))) const u32x2 *>((uintptr_t)addr);
+  return make_uint2(v.x, v.y);
+}
 
 // NCH: 1 KiB code chunks per row; D: rows a wavefront handles at once; G:
 // groups of D rows whose codes are in flight; T: threads per workgroup.
@@ -149,19 +168,27 @@ __global__ __launch_bounds__(T) void gemv_1x16_slice_kernel(SliceArgs A) {
   if (tid < 2) *reinterpret_cast<uint2 *>(table + (size_t)(kSlEntries + tid) * 8) = make_uint2(0, 0);
   __syncthreads();
 
-  // lanes past the end of a row read no codes: their words become all ones,
-  // which the slice test sends to the zero entry
-  uint32_t valid[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) valid[c] = (uint32_t)c * 1024u + lane_off < row_bytes ? 0u : ~0u;
+  // lanes past the end of a row read no codes (zero words): their key is all
+  // ones, so their t = w ^ key sends both halves to the zero entry
   const uint32_t key = (slice << 14) | (slice << 30);
+  uint32_t keyc[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) keyc[c] = (uint32_t)c * 1024u + lane_off < row_bytes ? key : ~0u;
+  const uint32_t tbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)table);
   float *const part = L.part + (size_t)member * L.out;
 
   // The D row sums of a group, reduced over the wavefront (totals in lane 63).
+  // Entry indexes: a packed 16-bit min of t; addresses: each half times 8
+  // plus the table's base, one multiply-add per half.
+  // Products: each looked-up half-codeword and the lane's four activations
+  // go into a 4x4x4 matrix-core product; lane 4q + j gives row j of block q's
+  // A and column j of its B, so element j of that lane's accumulator (the
+  // block's diagonal) collects exactly the lane's own dot products. The other
+  // elements hold cross products of neighbouring lanes and are not read.
   auto group_sums = [&](const uint4 (&c4)[D][NCH], float (&sum)[D]) {
-    float a0[D], a1[D];
+    float4_t acc[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) a0[d] = a1[d] = 0.0f;
+    for (int d = 0; d < D; ++d) acc[d] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       uint2 e[D][8];
@@ -170,23 +197,29 @@ __global__ __launch_bounds__(T) void gemv_1x16_slice_kernel(SliceArgs A) {
         const uint32_t wd[4] = {c4[d][c].x, c4[d][c].y, c4[d][c].z, c4[d][c].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t t = (wd[k] ^ key) | valid[c];
-          const uint32_t lo = min(t & 0xFFFFu, (uint32_t)kSlEntries);
-          const uint32_t hi = min(t >> 16, (uint32_t)kSlEntries);
-          e[d][2 * k] = *reinterpret_cast<const uint2 *>(table + lo * 8u);
-          e[d][2 * k + 1] = *reinterpret_cast<const uint2 *>(table + hi * 8u);
+          const uint32_t m = __builtin_bit_cast(
+              uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, wd[k] ^ keyc[c]),
+                                                  u16x2_t{(uint16_t)kSlEntries, (uint16_t)kSlEntries}));
+          e[d][2 * k] = lds_load8(entry_addr_lo(m, tbase));
+          e[d][2 * k + 1] = lds_load8(entry_addr_hi(m, tbase));
         }
       }
 #pragma unroll
       for (int d = 0; d < D; ++d)
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          a0[d] = dot2(e[d][p].x, xf[c][p].x, a0[d]);
-          a1[d] = dot2(e[d][p].y, xf[c][p].y, a1[d]);
-        }
+        for (int p = 0; p < 8; ++p)
+          acc[d] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, e[d][p]),
+                                                      __builtin_bit_cast(half4_t, xf[c][p]), acc[d],
+                                                      0, 0, 0);
     }
 #pragma unroll
-    for (int d = 0; d < D; ++d) sum[d] = wave_sum_to_lane63(a0[d] + a1[d]);
+    for (int d = 0; d < D; ++d) {
+      // the quad's four diagonal elements, then the sum over the 16 quads
+      float v = dpp<kDppQuadBcast0>(acc[d][0]) + dpp<kDppQuadBcast1>(acc[d][1]);
+      v += dpp<kDppQuadBcast2>(acc[d][2]);
+      v += dpp<kDppQuadBcast3>(acc[d][3]);
+      sum[d] = quads_sum_to_lane63(v);
+    }
   };
   auto store_group = [&](int k, const float (&sum)[D]) {
     if (lane == 63) {
