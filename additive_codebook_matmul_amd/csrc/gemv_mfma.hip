@@ -27,10 +27,12 @@
 //   * the activations are copied to LDS once per workgroup (rows padded by 16
 //     bytes); B fragment reads of one activation row are broadcasts;
 //   * codes of NBUF tiles ahead are in flight (buffer loads, non-temporal).
-//     NBUF is 1 when no block has more than two tiles: a prefetch past the
-//     last tile is a load with an out-of-range offset, which returns zero but
-//     still occupies the texture-address unit that the real loads of every
-//     wave on the CU queue behind.
+//     When every block has at most four tiles (and they fit in registers),
+//     all of a block's tiles are loaded in the prologue and nothing is
+//     refilled (ALL): no tile waits for a load issued after the previous
+//     tile, and no prefetch runs past the last tile (a load with an
+//     out-of-range offset returns zero but still occupies the texture-address
+//     unit that the real loads of every wave on the CU queue behind).
 #include "aqlm_device.hpp"
 
 #include <atomic>
@@ -65,7 +67,7 @@ struct MfmaLayer {
   int blk_begin, blk_count;  // blocks [blk_begin, blk_begin + blk_count) serve this layer
 };
 
-template <int BATCH, int MAXC, int NBUF>
+template <int BATCH, int MAXC, int NBUF, bool ALL>
 __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) {
   __shared__ __attribute__((aligned(16))) uint8_t table[kMTable];
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -241,22 +243,30 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
     }
   };
 
-  // NBUF tiles per loop pass so that every code buffer index is static; each
-  // buffer is refilled with the codes NBUF tiles ahead right after its tile.
-  for (int i0 = 0; i0 < my_tiles; i0 += NBUF) {
+  if constexpr (ALL) {
+    // my_tiles <= NBUF: every tile was loaded in the prologue
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      if (i0 + u < my_tiles) {
-        tile(i0 + u, cw[u]);
-        load_tile(i0 + u + NBUF, cw[u]);
+    for (int u = 0; u < NBUF; ++u)
+      if (u < my_tiles) tile(u, cw[u]);
+  } else {
+    // NBUF tiles per loop pass so that every code buffer index is static;
+    // each buffer is refilled with the codes NBUF tiles ahead right after its
+    // tile
+    for (int i0 = 0; i0 < my_tiles; i0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        if (i0 + u < my_tiles) {
+          tile(i0 + u, cw[u]);
+          load_tile(i0 + u + NBUF, cw[u]);
+        }
       }
     }
   }
 }
 
-template <int BATCH, int MAXC, int NBUF>
+template <int BATCH, int MAXC, int NBUF, bool ALL>
 __global__ __launch_bounds__(kMBlock) void gemv_2x8_mfma_kernel(MfmaLayer L) {
-  gemv_2x8_mfma_body<BATCH, MAXC, NBUF>(L, blockIdx.x);
+  gemv_2x8_mfma_body<BATCH, MAXC, NBUF, ALL>(L, blockIdx.x);
 }
 
 constexpr int kMaxMfmaGroup = 16;
@@ -265,13 +275,13 @@ struct MfmaGroup {
   int n;
 };
 
-template <int BATCH, int MAXC, int NBUF>
+template <int BATCH, int MAXC, int NBUF, bool ALL>
 __global__ __launch_bounds__(kMBlock) void gemv_2x8_mfma_group_kernel(MfmaGroup G) {
   int l = 0;
 #pragma unroll 1
   for (int i = 1; i < G.n; ++i)
     if ((int)blockIdx.x >= G.layer[i].blk_begin) l = i;
-  gemv_2x8_mfma_body<BATCH, MAXC, NBUF>(G.layer[l], blockIdx.x - G.layer[l].blk_begin);
+  gemv_2x8_mfma_body<BATCH, MAXC, NBUF, ALL>(G.layer[l], blockIdx.x - G.layer[l].blk_begin);
 }
 
 // Raise the dynamic LDS limit of a kernel once per device.
@@ -290,10 +300,10 @@ hipError_t allow_lds(K kernel, size_t bytes, std::atomic<uint64_t> &done) {
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-template <int BATCH, int MAXC, int NBUF>
+template <int BATCH, int MAXC, int NBUF, bool ALL>
 hipError_t launch_one(const MfmaLayer &L, hipStream_t stream) {
   static std::atomic<uint64_t> done{0};
-  auto k = gemv_2x8_mfma_kernel<BATCH, MAXC, NBUF>;
+  auto k = gemv_2x8_mfma_kernel<BATCH, MAXC, NBUF, ALL>;
   hipError_t e = allow_lds(k, kMaxLds - kMTable, done);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(L.blk_count), dim3(kMBlock), mfma_dyn_lds_bytes(BATCH, L.in), stream,
@@ -301,14 +311,48 @@ hipError_t launch_one(const MfmaLayer &L, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BATCH, int MAXC, int NBUF>
+template <int BATCH, int MAXC, int NBUF, bool ALL>
 hipError_t launch_group(const MfmaGroup &G, int blocks, size_t lds, hipStream_t stream) {
   static std::atomic<uint64_t> done{0};
-  auto k = gemv_2x8_mfma_group_kernel<BATCH, MAXC, NBUF>;
+  auto k = gemv_2x8_mfma_group_kernel<BATCH, MAXC, NBUF, ALL>;
   hipError_t e = allow_lds(k, kMaxLds - kMTable, done);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(blocks), dim3(kMBlock), lds - kMTable, stream, G);
   return hipGetLastError();
+}
+
+// The launches for the NBUF code that nbuf_for returns (-NBUF: ALL).
+template <int BATCH, int MAXC>
+hipError_t launch_one_nb(const MfmaLayer &L, int code, hipStream_t stream) {
+  switch (code) {
+    case -1: return launch_one<BATCH, MAXC, 1, true>(L, stream);
+    case -2: if constexpr (2 * MAXC <= 16) return launch_one<BATCH, MAXC, 2, true>(L, stream); break;
+    case -3: if constexpr (3 * MAXC <= 16) return launch_one<BATCH, MAXC, 3, true>(L, stream); break;
+    case -4: if constexpr (4 * MAXC <= 16) return launch_one<BATCH, MAXC, 4, true>(L, stream); break;
+    case 1: return launch_one<BATCH, MAXC, 1, false>(L, stream);
+    case 2: return launch_one<BATCH, MAXC, 2, false>(L, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BATCH, int MAXC>
+hipError_t launch_group_nb(const MfmaGroup &G, int blocks, size_t lds, int code,
+                           hipStream_t stream) {
+  switch (code) {
+    case -1: return launch_group<BATCH, MAXC, 1, true>(G, blocks, lds, stream);
+    case -2:
+      if constexpr (2 * MAXC <= 16) return launch_group<BATCH, MAXC, 2, true>(G, blocks, lds, stream);
+      break;
+    case -3:
+      if constexpr (3 * MAXC <= 16) return launch_group<BATCH, MAXC, 3, true>(G, blocks, lds, stream);
+      break;
+    case -4:
+      if constexpr (4 * MAXC <= 16) return launch_group<BATCH, MAXC, 4, true>(G, blocks, lds, stream);
+      break;
+    case 1: return launch_group<BATCH, MAXC, 1, false>(G, blocks, lds, stream);
+    case 2: return launch_group<BATCH, MAXC, 2, false>(G, blocks, lds, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Chunk-per-wave class: MAXC >= ceil(chunks / 8).
@@ -320,9 +364,15 @@ int mfma_class(int64_t nch) {
   return -1;
 }
 
-// Tiles of codes in flight per wave: one when no block has more than two
-// tiles (a deeper prefetch would only issue out-of-range loads), else two.
-constexpr int nbuf_for(int max_tiles_per_block) { return max_tiles_per_block <= 2 ? 1 : 2; }
+// Tiles of codes in flight per wave: every tile of the block (ALL) when a
+// block has at most four and they take at most 16 code registers of 16 bytes
+// per lane; else one when no block has more than two tiles (a deeper prefetch
+// would only issue out-of-range loads), else two. Returns NBUF, or -NBUF for
+// ALL.
+constexpr int nbuf_for(int max_tiles_per_block, int maxc) {
+  if (max_tiles_per_block <= 4 && max_tiles_per_block * maxc <= 16) return -max_tiles_per_block;
+  return max_tiles_per_block <= 2 ? 1 : 2;
+}
 
 int device_cus() {
   int dev = 0, cus = 256;
@@ -358,12 +408,12 @@ hipError_t launch_mfma_batch(const LayerDesc &L, const uint16_t *x, int batch, u
   if (blocks < min_blocks) blocks = min_blocks;
   MfmaLayer M{static_cast<const uint8_t *>(L.codes), L.books, L.scales, x, y, (int)L.out, (int)L.in,
               (int)L.groups, batch, 0, blocks};
-  const bool deep = nbuf_for((ntiles + blocks - 1) / blocks) == 2;
+  const int per_block = (ntiles + blocks - 1) / blocks;
   switch (mfma_class(L.groups / 32)) {
-    case 0: return deep ? launch_one<BATCH, 2, 2>(M, stream) : launch_one<BATCH, 2, 1>(M, stream);
-    case 1: return deep ? launch_one<BATCH, 4, 2>(M, stream) : launch_one<BATCH, 4, 1>(M, stream);
-    case 2: return deep ? launch_one<BATCH, 8, 2>(M, stream) : launch_one<BATCH, 8, 1>(M, stream);
-    case 3: return deep ? launch_one<BATCH, 16, 2>(M, stream) : launch_one<BATCH, 16, 1>(M, stream);
+    case 0: return launch_one_nb<BATCH, 2>(M, nbuf_for(per_block, 2), stream);
+    case 1: return launch_one_nb<BATCH, 4>(M, nbuf_for(per_block, 4), stream);
+    case 2: return launch_one_nb<BATCH, 8>(M, nbuf_for(per_block, 8), stream);
+    case 3: return launch_one_nb<BATCH, 16>(M, nbuf_for(per_block, 16), stream);
   }
   return hipErrorInvalidValue;
 }
@@ -402,8 +452,7 @@ hipError_t launch_mfma_group(const LayerDesc *const *Ls, const uint16_t *const *
                            (int)L.out, (int)L.in, (int)L.groups, batch, begin, blocks};
     begin += blocks;
   }
-  return nbuf_for(max_per_block) == 2 ? launch_group<BATCH, MAXC, 2>(G, begin, lds, stream)
-                                      : launch_group<BATCH, MAXC, 1>(G, begin, lds, stream);
+  return launch_group_nb<BATCH, MAXC>(G, begin, lds, nbuf_for(max_per_block, MAXC), stream);
 }
 
 template <int BATCH>
