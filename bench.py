@@ -83,7 +83,8 @@ def _parse():
                    help="timed steps (one step: 32 blocks x 7 layers, one token)")
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--layer-iters", type=int, default=200,
-                   help="launches per layer for the per-layer tables of --workload")
+                   help="launches per layer (at least two replays of the rotated copies) for "
+                        "the per-layer tables of --workload")
     p.add_argument("--schemes", default="2x8,1x16",
                    help="schemes of the headline run; the first one listed gives the "
                         "reported value (default 2x8)")
@@ -279,7 +280,7 @@ def per_layer_tables(args):
                 fn = lambda op=op: [getattr(L, op)(x, out=y) for L in Ls]
                 nbytes = b["codes"] + b["x"] + b["y"]
             g = _capture(torch, fn)
-            reps = max(2, 200 // copies)
+            reps = max(2, args.layer_iters // copies)
             us = 1e3 * _time_graph(torch, g, reps) / copies
             row = {"layer": layer.name, "out": layer.out_features, "in": layer.in_features,
                    "scheme": layer.scheme.name, "packed_codes": layer.packed, "batch": batch,
