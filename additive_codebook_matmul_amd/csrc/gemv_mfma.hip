@@ -27,10 +27,10 @@
 //   * the activations are copied to LDS once per workgroup (rows padded by 16
 //     bytes); B fragment reads of one activation row are broadcasts;
 //   * codes of NBUF tiles ahead are in flight (buffer loads, non-temporal).
-//     When every block has at most four tiles (and they fit in registers),
+//     When every block has at most two tiles (and they fit in registers),
 //     all of a block's tiles are loaded in the prologue and nothing is
-//     refilled (ALL): no tile waits for a load issued after the previous
-//     tile, and no prefetch runs past the last tile (a load with an
+//     refilled (ALL): the second tile does not wait for a load issued after
+//     the first, and no prefetch runs past the last tile (a load with an
 //     out-of-range offset returns zero but still occupies the texture-address
 //     unit that the real loads of every wave on the CU queue behind).
 #include "aqlm_device.hpp"
@@ -327,9 +327,6 @@ hipError_t launch_one_nb(const MfmaLayer &L, int code, hipStream_t stream) {
   switch (code) {
     case -1: return launch_one<BATCH, MAXC, 1, true>(L, stream);
     case -2: if constexpr (2 * MAXC <= 16) return launch_one<BATCH, MAXC, 2, true>(L, stream); break;
-    case -3: if constexpr (3 * MAXC <= 16) return launch_one<BATCH, MAXC, 3, true>(L, stream); break;
-    case -4: if constexpr (4 * MAXC <= 16) return launch_one<BATCH, MAXC, 4, true>(L, stream); break;
-    case 1: return launch_one<BATCH, MAXC, 1, false>(L, stream);
     case 2: return launch_one<BATCH, MAXC, 2, false>(L, stream);
   }
   return hipErrorInvalidValue;
@@ -343,13 +340,6 @@ hipError_t launch_group_nb(const MfmaGroup &G, int blocks, size_t lds, int code,
     case -2:
       if constexpr (2 * MAXC <= 16) return launch_group<BATCH, MAXC, 2, true>(G, blocks, lds, stream);
       break;
-    case -3:
-      if constexpr (3 * MAXC <= 16) return launch_group<BATCH, MAXC, 3, true>(G, blocks, lds, stream);
-      break;
-    case -4:
-      if constexpr (4 * MAXC <= 16) return launch_group<BATCH, MAXC, 4, true>(G, blocks, lds, stream);
-      break;
-    case 1: return launch_group<BATCH, MAXC, 1, false>(G, blocks, lds, stream);
     case 2: return launch_group<BATCH, MAXC, 2, false>(G, blocks, lds, stream);
   }
   return hipErrorInvalidValue;
@@ -365,13 +355,13 @@ int mfma_class(int64_t nch) {
 }
 
 // Tiles of codes in flight per wave: every tile of the block (ALL) when a
-// block has at most four and they take at most 16 code registers of 16 bytes
-// per lane; else one when no block has more than two tiles (a deeper prefetch
-// would only issue out-of-range loads), else two. Returns NBUF, or -NBUF for
-// ALL.
+// block has at most two (q,k,v call 8.8 -> 8.1 us, o 4.2 -> 4.0, down
+// 8.0 -> 7.6 against one tile ahead), else two, refilled after each tile
+// (three-tile blocks: all three up front took the gate,up call from 10.8 to
+// 11.3 us). Returns NBUF, or -NBUF for ALL.
 constexpr int nbuf_for(int max_tiles_per_block, int maxc) {
-  if (max_tiles_per_block <= 4 && max_tiles_per_block * maxc <= 16) return -max_tiles_per_block;
-  return max_tiles_per_block <= 2 ? 1 : 2;
+  if (max_tiles_per_block <= 2 && max_tiles_per_block * maxc <= 16) return -max_tiles_per_block;
+  return 2;
 }
 
 int device_cus() {
