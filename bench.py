@@ -132,10 +132,13 @@ def _median_time(fn, runs=3):
     return statistics.median(ts)
 
 
+CPU_RUNS = 8  # timed runs per layer and oracle step
+
+
 def cpu_baseline(layers_np):
     """The CPU oracle on the seven layers of one block: O1 decode (numpy,
     float32, single-threaded) and O2 product (float64 BLAS) timed separately
-    per layer, median of three runs each."""
+    per layer, median of CPU_RUNS runs each (about 11 s of CPU work in all)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -148,8 +151,8 @@ def cpu_baseline(layers_np):
     per_layer = {}
     for (layer, d, x, nbytes) in layers_np:
         w = oracle.decode(d.codes, d.codebooks, d.scales)
-        td = _median_time(lambda: oracle.decode(d.codes, d.codebooks, d.scales))
-        tp = _median_time(lambda: oracle.product(x, w))
+        td = _median_time(lambda: oracle.decode(d.codes, d.codebooks, d.scales), CPU_RUNS)
+        tp = _median_time(lambda: oracle.product(x, w), CPU_RUNS)
         t_dec += td
         t_prod += tp
         block_bytes += nbytes
@@ -162,7 +165,7 @@ def cpu_baseline(layers_np):
         "kind": "oracle",
         "sample": f"one Llama-2-7B block (seven layers, batch 1) of the scheme: O1 decode "
                   f"{1e3 * t_dec:.0f} ms, O2 product {1e3 * t_prod:.0f} ms per block, each the "
-                  f"median of 3 runs per layer ({wall:.1f} s in all); decode is single-threaded "
+                  f"median of {CPU_RUNS} runs per layer ({wall:.1f} s in all); decode is single-threaded "
                   f"numpy, the float64 product uses BLAS with up to {blas_threads} threads",
         "per_layer": per_layer,
     }
