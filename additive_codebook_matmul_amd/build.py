@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libaqlm_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ("api.hip", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemv_slice.hip", "gemm.hip",
-           "gemm_mid.hip", "general.hip", "encode.hip")
+           "gemm_mid.hip", "gemm_tile.hip", "general.hip", "encode.hip")
 ARCH = "gfx950"
 HOST_SOURCE = "host_gemv.cpp"
 HOST_LIB_PATH = os.path.join(PKG_DIR, "libaqlm_host.so")

@@ -653,6 +653,8 @@ bool skinny_fits(const LayerDesc &L, int64_t batch, int nt) {
 template <Scheme S>
 constexpr int wide_ni() { return S == Scheme::k2x8 ? 2 : 4; }
 
+
+
 // 32-bit byte offsets of the wide kernel: codes of 256 rows past the end and
 // activations of a whole block past the end must stay below 2^32.
 bool wide_fits(const LayerDesc &L, int64_t batch, int ni) {
@@ -686,6 +688,9 @@ hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int64_t batch, u
   if (batch <= 16 && skinny_fits(L, batch, 1)) return launch_skinny<S, 1>(L, x, batch, y, stream);
   if (batch <= kSkinnyMaxBatch && skinny_fits(L, batch, 2))
     return launch_skinny<S, 2>(L, x, batch, y, stream);
+  if constexpr (S == Scheme::k2x8) {
+    if (gemm_tile_preferred(L, batch)) return launch_gemm_tile(L, x, batch, y, stream);
+  }
   if (wide_fits(L, batch, wide_ni<S>())) return launch_wide<S, wide_ni<S>()>(L, x, batch, y, stream);
   // sizes past the 32-bit offsets of the tiled kernels: the general kernel
   // (64-bit indexing, exact fp16 weight tiles)
