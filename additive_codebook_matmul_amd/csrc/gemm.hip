@@ -688,9 +688,7 @@ hipError_t launch_scheme(const LayerDesc &L, const uint16_t *x, int64_t batch, u
   if (batch <= 16 && skinny_fits(L, batch, 1)) return launch_skinny<S, 1>(L, x, batch, y, stream);
   if (batch <= kSkinnyMaxBatch && skinny_fits(L, batch, 2))
     return launch_skinny<S, 2>(L, x, batch, y, stream);
-  if constexpr (S == Scheme::k2x8) {
-    if (gemm_tile_preferred(L, batch)) return launch_gemm_tile(L, x, batch, y, stream);
-  }
+  if (gemm_tile_preferred(L, batch)) return launch_gemm_tile(L, x, batch, y, stream);
   if (wide_fits(L, batch, wide_ni<S>())) return launch_wide<S, wide_ni<S>()>(L, x, batch, y, stream);
   // sizes past the 32-bit offsets of the tiled kernels: the general kernel
   // (64-bit indexing, exact fp16 weight tiles)

@@ -1,32 +1,51 @@
-// Batched 2x8 product for many activation rows, with each weight tile decoded
-// once into LDS and shared by all wavefronts of the block.
+// Batched product for many activation rows, with each weight tile decoded
+// once into LDS and shared by all wavefronts of the block (the dedicated
+// schemes 2x8, 1x16 and 1x16 g16).
 //
 // The wide kernel (gemm.hip) decodes every wavefront's own rows straight into
 // MFMA operand registers and reuses each decoded operand for the block's
-// 32 * NI activation rows, so at 2048 rows every weight is decoded 32 times
-// and the random codeword reads of the decode keep the LDS busier than the
-// matrix cores. Here a block owns 128 output rows and 256 activation rows:
-//   * per K block of 8 groups (64 inputs) the block's 256 threads decode the
-//     128 x 64 weight tile once (thread t: row t / 2, groups 4 (t % 2) ..
-//     4 (t % 2) + 3; the fp16 sum of the two codewords from an 8 KiB LDS copy
-//     of the codebooks, as in every 2x8 matrix-core tile) into an LDS tile, and
-//     stage the 256 x 64 activation tile next to it; both are double-buffered
-//     and filled for K block kb + 1 while the matrix cores work on kb;
-//   * wavefront w multiplies all 128 rows with activation rows 64 w .. 64 w +
-//     63: 4 x 2 tiles of v_mfma_f32_32x32x16_f16 per 16-input step, both
+// 32 * NI activation rows, so at 2048 rows every weight is decoded 16 to 32
+// times: for 2x8 the random codeword reads of the decode keep the LDS busier
+// than the matrix cores, for 1x16 the codeword gathers from L2 bound the
+// kernel. Here a block of 512 threads owns 128 output rows and 256
+// activation rows, and its wavefronts split into two roles that meet at one
+// barrier per K block of 64 inputs:
+//   * four filling wavefronts decode K block kb + 1's 128 x 64 weight tile
+//     once (thread p: row p / 2, inputs 32 (p % 2) .. + 31, i.e. four
+//     16-byte chunks) into one of two LDS tiles and stage its 256 x 64
+//     activation tile next to it, while the matrix cores work on kb. A 2x8
+//     chunk is the fp16 sum of the two codewords read from an 8 KiB LDS copy
+//     of the codebooks, as in every 2x8 matrix-core tile; a 1x16 chunk is the
+//     codeword (g 8) or half of it (g 16), gathered from the L2-resident
+//     codebook two K blocks ahead. Codes are loaded four K blocks ahead,
+//     activations four (1x16) or two (2x8) K blocks ahead, all with
+//     unconditional buffer loads (out of range offsets read zero: rows past
+//     the end decode to codeword 0 or codeword sums that are never stored,
+//     activation rows past the end are zero);
+//   * four multiplying wavefronts, one per SIMD next to a filling one: wave
+//     w multiplies all 128 rows with activation rows 64 w .. 64 w + 63,
+//     4 x 2 tiles of v_mfma_f32_32x32x16_f16 per 16-input step, both
 //     operands read from LDS (one 16-byte read per lane and tile);
 //   * tile rows are 128 bytes; 16-byte chunk j of row r is stored at chunk
 //     j ^ ((r >> 1) & 7), so the 16 lanes of an LDS pass (16 consecutive rows,
 //     one chunk) and the decode and staging writes touch 16 distinct 16-byte
 //     bank groups;
-//   * codes are loaded four K blocks ahead (8 bytes per thread and K block),
-//     activations two K blocks ahead, with unconditional buffer loads (out of
-//     range offsets read zero: rows past the end decode to codeword sums that
-//     are never stored, activation rows past the end are zero);
 //   * the row scale multiplies the float32 accumulator in the epilogue; the
-//     overflow guard of the fp16 codeword sum is the one of the other tiles.
-// A weight is decoded once per 256 activation rows (the wide kernel: per 64),
-// and the LDS traffic per MFMA is about 1.1 conflict-free 16-byte reads.
+//     overflow guard of the 2x8 fp16 codeword sum is the one of the other
+//     tiles (a single 1x16 codeword is an fp16 value already).
+// A weight is decoded once per 256 activation rows, and the LDS traffic per
+// MFMA is about 1.1 conflict-free 16-byte reads.
+//
+// Where the time goes (2x8, 11008 x 4096 at 2048 rows, same-box timings of
+// copies with parts of the work removed): the MFMAs alone 135 us, with their
+// LDS operand reads 176 us, the filling wavefronts alone 157-185 us, all of
+// it 261-276 us; 1x16 g16: the gathers alone 155 us (the L2 gather rate).
+// Measured and not kept: the activation operand loaded by the multiplying
+// wavefronts from global memory one K block ahead (no LDS staging; the
+// fill drops to 108 us, the multiply stalls on the loads: 291 us), operand
+// reads pinned two steps ahead of their MFMAs (no gain), the 2x8 codebooks
+// in a 64 KiB bank-spread table (conflict-free decode reads; no gain), one
+// role for all 256 threads of a four-wavefront block (301 us).
 #include <atomic>
 #include <type_traits>
 
@@ -35,57 +54,61 @@
 namespace aqlm {
 namespace {
 
-constexpr int kTThreads = 256;
+constexpr int kTThreads = 512;     // 4 multiplying + 4 filling wavefronts
 constexpr int kTWaves = kTThreads / 64;
+constexpr int kTFill = 256;        // threads of the filling wavefronts
 constexpr int kTBM = 128;          // output rows per block
-constexpr int kTBN = 256;          // activation rows per block (64 per wavefront)
-constexpr int kTKG = 8;            // groups per K block: 64 inputs
-constexpr int kTCodeDepth = 4;     // K blocks of codes in flight; the loop is unrolled to match
+constexpr int kTBN = 256;          // activation rows per block (64 per multiplying wavefront)
+constexpr int kTKIn = 64;          // inputs per K block
+constexpr int kTCodeDepth = 4;     // K blocks of codes in flight; the fill loop is unrolled to match
 constexpr uint32_t kTOOB = 0x80000000u;
-constexpr int kTBooksBytes = 512 * 16;
 constexpr int kTWBytes = kTBM * 128;  // 128 rows x 64 halves
 constexpr int kTXBytes = kTBN * 128;  // 256 activation rows x 64 halves
-constexpr int kTLdsBytes = kTBooksBytes + 2 * kTWBytes + 2 * kTXBytes + kTWaves * 4;
+
+// Per scheme: codeword length, code bytes a fill thread takes per K block
+// (half of a row's), bytes of the LDS codebook copy.
+template <Scheme S> struct TileScheme {
+  static constexpr int G = S == Scheme::k1x16g16 ? 16 : 8;
+  static constexpr int KG = kTKIn / G;                 // groups per K block
+  static constexpr int CB = KG * kCodeBytesPerGroup / 2;
+  static constexpr int BOOKS = S == Scheme::k2x8 ? 512 * 16 : 0;
+  static constexpr int LDS = BOOKS + 2 * kTWBytes + 2 * kTXBytes + kTWaves * 4;
+};
 
 // Byte offset of 16-byte chunk j of tile row r.
 __device__ __forceinline__ uint32_t tile_off(int r, int j) {
   return (uint32_t)r * 128u + (uint32_t)((j ^ ((r >> 1) & 7)) << 4);
 }
 
-__global__ __launch_bounds__(kTThreads) void gemm_tile_2x8_kernel(
-    const uint8_t *__restrict__ codes, const uint4 *__restrict__ books,
-    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, uint16_t *__restrict__ y,
-    int out, int in, int groups, int batch, uint32_t codes_bytes, uint32_t x_bytes) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint4 *lbooks = reinterpret_cast<uint4 *>(lds);
-  uint8_t *wt = lds + kTBooksBytes;  // [2][kTWBytes]
-  uint8_t *xt = wt + 2 * kTWBytes;   // [2][kTXBytes]
-  uint32_t *big_flags = reinterpret_cast<uint32_t *>(xt + 2 * kTXBytes);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hl = lane >> 5;
-  const int row0 = blockIdx.x * kTBM;
-  const int tok0 = blockIdx.y * kTBN;
+// The filling wavefronts (threads p = 0 .. 255 of them): decode K block
+// kb + 1's weight tile and stage its activation tile into the LDS buffers
+// the multiplying wavefronts are not reading, one barrier per K block.
+template <Scheme S>
+__device__ __forceinline__ void tile_fill(const int p, uint8_t *__restrict__ wt,
+                                          uint8_t *__restrict__ xt, const uint4 *lbooks,
+                                          const Rsrc crs, const Rsrc xrs, const Rsrc brs,
+                                          int row0, int tok0, int out, int in, int groups,
+                                          int batch) {
+  using C = TileScheme<S>;
   const uint32_t row_bytes = (uint32_t)groups * 2u;
-  const Rsrc crs = make_rsrc(codes, codes_bytes);
-  const Rsrc xrs = make_rsrc(x, x_bytes);
-  const int nkb = groups / kTKG;
-
-  // decode role: row dr of the tile, groups 4 dh .. 4 dh + 3 of the K block
-  const int dr = tid >> 1, dh = tid & 1;
+  const int nkb = groups / C::KG;
+  // decode role: row dr of the tile, inputs 32 dh .. 32 dh + 31 of the K
+  // block (tile chunks 4 dh .. 4 dh + 3): 2x8 and 1x16 four groups, 1x16 g16
+  // two
+  const int dr = p >> 1, dh = p & 1;
   const bool dr_ok = row0 + dr < out;
-  const uint32_t coff = (uint32_t)(row0 + dr) * row_bytes + (uint32_t)dh * 8u;
+  const uint32_t coff = (uint32_t)(row0 + dr) * row_bytes + (uint32_t)dh * C::CB;
   auto load_codes = [&](int kb) -> uint2 {
-    return buf_load8(crs, (dr_ok && kb < nkb) ? coff + (uint32_t)kb * 16u : kTOOB);
+    const uint32_t off = (dr_ok && kb < nkb) ? coff + (uint32_t)kb * (2 * C::CB) : kTOOB;
+    if constexpr (C::CB == 8) return buf_load8(crs, off);
+    else return make_uint2(buf_load4(crs, off), 0u);
   };
-  // staging role: chunks c = tid + 256 i of the activation tile, activation
+  // staging role: chunks c = p + 256 i of the activation tile, activation
   // row c / 8, 16-byte chunk c % 8 (a row's 128 bytes by 8 consecutive lanes)
   auto load_x = [&](int kb, uint4 (&xr)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int c = tid + i * kTThreads;
+      const int c = p + i * kTFill;
       const int t = c >> 3, j = c & 7;
       const bool ok = tok0 + t < batch && kb < nkb;
       xr[i] = buf_load16(
@@ -97,21 +120,120 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_2x8_kernel(
     uint8_t *dst = xt + buf * kTXBytes;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int c = tid + i * kTThreads;
+      const int c = p + i * kTFill;
       *reinterpret_cast<uint4 *>(dst + tile_off(c >> 3, c & 7)) = xr[i];
     }
   };
-  auto decode = [&](int buf, uint2 cw) {
-    uint8_t *dst = wt + buf * kTWBytes;
+  // 2x8: the eight codewords of four groups read from the LDS codebooks at
+  // the start of a K block's fill, summed into the tile at its end
+  auto read_books = [&](uint2 cw, uint4 (&bk)[8]) {
     const uint32_t w[2] = {cw.x, cw.y};
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t code = (w[g >> 1] >> ((g & 1) * 16)) & 0xFFFFu;
-      const uint4 v = hadd8(lbooks[code & 0xFFu], lbooks[256 + (code >> 8)]);
-      *reinterpret_cast<uint4 *>(dst + tile_off(dr, dh * 4 + g)) = v;
+      bk[2 * g] = lbooks[code & 0xFFu];
+      bk[2 * g + 1] = lbooks[256 + (code >> 8)];
     }
   };
+  auto put_sums = [&](int buf, const uint4 (&bk)[8]) {
+    uint8_t *dst = wt + buf * kTWBytes;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<uint4 *>(dst + tile_off(dr, dh * 4 + g)) = hadd8(bk[2 * g], bk[2 * g + 1]);
+  };
+  // 1x16: the four chunks gathered from the codebook (16 bytes per codeword
+  // for g 8, 32 for g 16) two K blocks ahead, then written into the tile
+  auto gather = [&](uint2 cw, uint4 (&gv)[4]) {
+    const uint32_t w[2] = {cw.x, cw.y};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (C::G == 8) {
+        const uint32_t code = (w[g >> 1] >> ((g & 1) * 16)) & 0xFFFFu;
+        gv[g] = buf_load16(brs, code * 16u);
+      } else {
+        const uint32_t code = (w[0] >> ((g >> 1) * 16)) & 0xFFFFu;
+        gv[g] = buf_load16(brs, code * 32u + (uint32_t)(g & 1) * 16u);
+      }
+    }
+  };
+  auto put = [&](int buf, const uint4 (&gv)[4]) {
+    uint8_t *dst = wt + buf * kTWBytes;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *reinterpret_cast<uint4 *>(dst + tile_off(dr, dh * 4 + g)) = gv[g];
+  };
 
+  // One filling wavefront per SIMD has nothing to hide its load latency
+  // behind but its own later work, so the activation loads run four K
+  // blocks ahead (K blocks kb + 1 .. kb + 4 in flight, slot k % 4) and the
+  // 1x16 codeword gathers two. Codes come four K blocks before their first
+  // use.
+  uint2 cq[kTCodeDepth];
+#pragma unroll
+  for (int i = 0; i < kTCodeDepth; ++i) cq[i] = load_codes(i);
+  uint4 xr[4][8];
+  uint4 gv[2][4];
+  if constexpr (S != Scheme::k2x8) {
+    gather(cq[0], gv[0]);
+    gather(cq[1], gv[1]);
+    cq[0] = load_codes(4);
+    cq[1] = load_codes(5);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_x(i, xr[i]);
+  if constexpr (S == Scheme::k2x8) {
+    uint4 bk[8];
+    read_books(cq[0], bk);
+    cq[0] = load_codes(4);
+    put_sums(0, bk);
+  } else {
+    put(0, gv[0]);
+  }
+  store_x(0, xr[0]);
+  __syncthreads();
+
+  // K block kb (the multiply of kb runs meanwhile): fill the other buffers
+  // with kb + 1, issuing the loads of later K blocks into the slots K block
+  // kb has left, barrier. The last K blocks fill buffers with the zeros of
+  // out-of-range loads (codeword 0 for 1x16); nothing reads them.
+  auto iter = [&](int kb, auto kc) {
+    constexpr int K = decltype(kc)::value;  // kb % 4
+    if constexpr (S == Scheme::k2x8) {
+      constexpr int N = (K + 1) % kTCodeDepth;
+      uint4 bk[8];
+      read_books(cq[N], bk);  // K block kb + 1
+      cq[N] = load_codes(kb + 5);
+      load_x(kb + 4, xr[K]);
+      store_x((K + 1) & 1, xr[(K + 1) % 4]);
+      put_sums((K + 1) & 1, bk);
+    } else {
+      constexpr int N = (K + 2) % kTCodeDepth;
+      gather(cq[N], gv[K & 1]);  // K block kb + 2
+      cq[N] = load_codes(kb + 6);
+      load_x(kb + 4, xr[K]);
+      put((K + 1) & 1, gv[(K + 1) & 1]);
+      store_x((K + 1) & 1, xr[(K + 1) % 4]);
+    }
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb + 4 <= nkb; kb += 4) {
+    iter(kb, std::integral_constant<int, 0>{});
+    iter(kb + 1, std::integral_constant<int, 1>{});
+    iter(kb + 2, std::integral_constant<int, 2>{});
+    iter(kb + 3, std::integral_constant<int, 3>{});
+  }
+  if (kb < nkb) iter(kb, std::integral_constant<int, 0>{});
+  if (kb + 1 < nkb) iter(kb + 1, std::integral_constant<int, 1>{});
+  if (kb + 2 < nkb) iter(kb + 2, std::integral_constant<int, 2>{});
+}
+
+// The multiplying wavefronts (w = 0 .. 3): all 128 rows of the block times
+// activation rows 64 w .. 64 w + 63, one barrier per K block, then y.
+__device__ __forceinline__ void tile_multiply(const int w, const int lane, const uint8_t *wt,
+                                              const uint8_t *xt, const uint16_t *__restrict__ scales,
+                                              uint16_t *__restrict__ y, int row0, int tok0,
+                                              int out, int batch, int nkb, float total_mul) {
+  const int l32 = lane & 31, hl = lane >> 5;
   float16_t acc[4][2];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -122,8 +244,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_2x8_kernel(
 
   // the MFMAs of one K block from LDS buffer buf: in step s the lane half hl
   // feeds chunk 2 s + hl of the K block, in A and in B alike; step s + 1's
-  // operand reads are issued before step s's MFMAs. (Spreading the next K
-  // block's decode and staging between these MFMAs measured the same.)
+  // operand reads are issued before step s's MFMAs.
   auto compute = [&](int buf) {
     const uint8_t *W = wt + buf * kTWBytes;
     const uint8_t *X = xt + buf * kTXBytes;
@@ -135,7 +256,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_2x8_kernel(
         a[slot][mi] = *reinterpret_cast<const uint4 *>(W + tile_off(mi * 32 + l32, j));
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni)
-        b[slot][ni] = *reinterpret_cast<const uint4 *>(X + tile_off(wave * 64 + ni * 32 + l32, j));
+        b[slot][ni] = *reinterpret_cast<const uint4 *>(X + tile_off(w * 64 + ni * 32 + l32, j));
     };
     reads(0, 0);
 #pragma unroll
@@ -156,63 +277,18 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_2x8_kernel(
     }
   };
 
-  // Prologue: codes of K blocks 0 .. 3, activations of K blocks 0 and 1, the
-  // codebooks into LDS, K block 0's activations into LDS, then K block 0's
-  // weight tile.
-  uint2 cq[kTCodeDepth];
-#pragma unroll
-  for (int i = 0; i < kTCodeDepth; ++i) cq[i] = load_codes(i);
-  uint4 xr[2][8];
-  load_x(0, xr[0]);
-  load_x(1, xr[1]);
-  bool large = false;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint4 v = books[tid + i * kTThreads];
-    large |= has_large_half(v);
-    lbooks[tid + i * kTThreads] = v;
-  }
-  publish_flag(big_flags, large);
-  store_x(0, xr[0]);
-  __syncthreads();
-  // codebooks large enough for the fp16 codeword sum to overflow: halve the
-  // table, double the totals (overflow guard, aqlm_device.hpp)
-  float total_mul = 1.0f;
-  if (read_flag(big_flags, kTWaves)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) lbooks[tid + i * kTThreads] = hhalf8(lbooks[tid + i * kTThreads]);
-    __syncthreads();
-    total_mul = 2.0f;
-  }
-  decode(0, cq[0]);
-  cq[0] = load_codes(kTCodeDepth);
-  __syncthreads();
-
-  // K block kb: prefetch the activations of kb + 2, multiply kb, fill the
-  // other buffers with kb + 1 (decode from code slot (kb + 1) % 4, then refill
-  // that slot with kb + 5), barrier.
-  auto iter = [&](int kb, auto kc) {
-    constexpr int K = decltype(kc)::value;  // kb % 4
-    constexpr int N = (K + 1) % kTCodeDepth;
-    load_x(kb + 2, xr[K & 1]);
-    compute(K & 1);
-    // the last K block also fills the other buffers, with the zeros of the
-    // out-of-range loads; nothing reads them
-    decode((K + 1) & 1, cq[N]);
-    store_x((K + 1) & 1, xr[(K + 1) & 1]);
-    cq[N] = load_codes(kb + 1 + kTCodeDepth);
-    __syncthreads();
-  };
+  __syncthreads();  // K block 0's tiles
   int kb = 0;
-  for (; kb + 4 <= nkb; kb += 4) {
-    iter(kb, std::integral_constant<int, 0>{});
-    iter(kb + 1, std::integral_constant<int, 1>{});
-    iter(kb + 2, std::integral_constant<int, 2>{});
-    iter(kb + 3, std::integral_constant<int, 3>{});
+  for (; kb + 2 <= nkb; kb += 2) {
+    compute(0);
+    __syncthreads();
+    compute(1);
+    __syncthreads();
   }
-  if (kb < nkb) iter(kb, std::integral_constant<int, 0>{});
-  if (kb + 1 < nkb) iter(kb + 1, std::integral_constant<int, 1>{});
-  if (kb + 2 < nkb) iter(kb + 2, std::integral_constant<int, 2>{});
+  if (kb < nkb) {
+    compute(0);
+    __syncthreads();
+  }
 
   // Epilogue: lane holds activation row l32 of each 32 x 32 tile; register r
   // is output row 8 (r / 4) + 4 hl + r % 4, so registers 4 q .. 4 q + 3 are
@@ -222,7 +298,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_2x8_kernel(
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
-      const int tok = tok0 + wave * 64 + ni * 32 + l32;
+      const int tok = tok0 + w * 64 + ni * 32 + l32;
       if (tok >= batch) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -246,49 +322,112 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_2x8_kernel(
   }
 }
 
+template <Scheme S>
+__global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(
+    const uint8_t *__restrict__ codes, const uint4 *__restrict__ books,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ x, uint16_t *__restrict__ y,
+    int out, int in, int groups, int batch, uint32_t codes_bytes, uint32_t x_bytes) {
+  using C = TileScheme<S>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint4 *lbooks = reinterpret_cast<uint4 *>(lds);
+  uint8_t *wt = lds + C::BOOKS;      // [2][kTWBytes]
+  uint8_t *xt = wt + 2 * kTWBytes;   // [2][kTXBytes]
+  uint32_t *big_flags = reinterpret_cast<uint32_t *>(xt + 2 * kTXBytes);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = blockIdx.x * kTBM;
+  const int tok0 = blockIdx.y * kTBN;
+
+  // 2x8: the codebooks into LDS, one 16-byte entry per thread; codebooks
+  // large enough for the fp16 codeword sum to overflow are halved and the
+  // totals doubled (overflow guard, aqlm_device.hpp)
+  float total_mul = 1.0f;
+  if constexpr (S == Scheme::k2x8) {
+    const uint4 v = books[tid];
+    lbooks[tid] = v;
+    publish_flag(big_flags, has_large_half(v));
+    __syncthreads();
+    if (read_flag(big_flags, kTWaves)) {
+      lbooks[tid] = hhalf8(v);
+      total_mul = 2.0f;
+    }
+    __syncthreads();
+  }
+  // Both roles pass the same barriers: one after K block 0's tiles, one per
+  // K block after that.
+  if (wave >= kTWaves / 2) {
+    tile_fill<S>(tid - kTFill, wt, xt, lbooks, make_rsrc(codes, codes_bytes), make_rsrc(x, x_bytes),
+                 make_rsrc(books, (uint32_t)(65536 * C::G * 2)), row0, tok0, out, in, groups,
+                 batch);
+  } else {
+    tile_multiply(wave, tid & 63, wt, xt, scales, y, row0, tok0, out, batch, groups / C::KG,
+                  total_mul);
+  }
+}
+
 }  // namespace
 
-// True when the decoded-tile kernel serves this 2x8 layer and batch: whole
-// K blocks (groups a multiple of 8) and 32-bit byte offsets for the codes
-// (rows of one block past the end) and the activations (one block past the
-// end).
+// True when the decoded-tile kernel serves this layer and batch: a dedicated
+// scheme, whole K blocks (in a multiple of 64) and 32-bit byte offsets for the
+// codes (rows of one block past the end) and the activations (one block past
+// the end).
 bool gemm_tile_fits(const LayerDesc &L, int64_t batch) {
-  if (L.scheme != Scheme::k2x8 || L.groups % kTKG != 0) return false;
+  if (L.scheme == Scheme::kGeneral || L.packed || L.in % kTKIn != 0) return false;
   const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
   return (L.out + kTBM) * row_bytes + 4096 < (int64_t(1) << 31) &&
          (batch + kTBN) * L.in * 2 + 4096 < (int64_t(1) << 31);
 }
 
-// Where it runs instead of the wide tiles: from 1536 activation rows, when
-// its grid gives every CU a block at least once. Same-box timings of the
-// binding's gemm (2x8, wide tiles -> this kernel): 11008x4096 at 2048 rows
-// 329-332 -> 293-295 us, 4096x11008 at 2048 rows 273 -> 254-257 us; at 1024
-// rows 11008x4096 is even (172 -> 176 us) and 4096x11008, on 128 blocks,
-// slower (157 -> 203 us), at 256 rows 11008x4096 slower (67 -> 84 us).
+// Where it runs instead of the wide tiles: from 512 activation rows, when
+// its grid has at least 160 blocks. Same-box timings of the binding's gemm
+// (wide tiles -> this kernel, us):
+//                        512 rows      1024 rows     2048 rows
+//   2x8      11008x4096  99 -> 79      169 -> 158    301 -> 261..276
+//            4096x11008  61 -> 60      162 -> 173    260 -> 230..240
+//   1x16 g16 11008x4096  126 -> 86     254 -> 173    410 -> 298..312
+//            4096x11008  113 -> 112    214 -> 218    389 -> 274..289
+//   1x16     11008x4096  175 -> 105    345 -> 217    581 -> 370..380
+//            4096x11008  146 -> 141    272 -> 269    505 -> 343..354
+// (4096x11008 has 64 blocks at 512 rows and 128 at 1024); at 256 rows on
+// 11008x4096 (86 blocks) the 2x8 tile was slower (67 -> 84 us).
 bool gemm_tile_preferred(const LayerDesc &L, int64_t batch) {
-  if (batch < 1536 || !gemm_tile_fits(L, batch)) return false;
-  return ((L.out + kTBM - 1) / kTBM) * ((batch + kTBN - 1) / kTBN) >= 256;
+  if (batch < 512 || !gemm_tile_fits(L, batch)) return false;
+  return ((L.out + kTBM - 1) / kTBM) * ((batch + kTBN - 1) / kTBN) >= 160;
 }
 
-hipError_t launch_gemm_tile(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
-                            hipStream_t stream) {
+namespace {
+template <Scheme S>
+hipError_t launch_tile(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
+                       hipStream_t stream) {
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = uint64_t(1) << (dev & 63);
   if (dev >= 64 || !(raised.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tile_2x8_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kTLdsBytes);
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_tile_kernel<S>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, TileScheme<S>::LDS);
     if (e != hipSuccess) return e;
     raised.fetch_or(bit, std::memory_order_acq_rel);
   }
   const dim3 grid((unsigned)((L.out + kTBM - 1) / kTBM), (unsigned)((batch + kTBN - 1) / kTBN));
-  hipLaunchKernelGGL(gemm_tile_2x8_kernel, grid, dim3(kTThreads), kTLdsBytes, stream,
+  hipLaunchKernelGGL(gemm_tile_kernel<S>, grid, dim3(kTThreads), TileScheme<S>::LDS, stream,
                      static_cast<const uint8_t *>(L.codes), reinterpret_cast<const uint4 *>(L.books),
                      L.scales, x, y, (int)L.out, (int)L.in, (int)L.groups, (int)batch,
                      (uint32_t)(L.out * L.groups * kCodeBytesPerGroup), (uint32_t)(batch * L.in * 2));
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_tile(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
+                            hipStream_t stream) {
+  switch (L.scheme) {
+    case Scheme::k2x8: return launch_tile<Scheme::k2x8>(L, x, batch, y, stream);
+    case Scheme::k1x16: return launch_tile<Scheme::k1x16>(L, x, batch, y, stream);
+    case Scheme::k1x16g16: return launch_tile<Scheme::k1x16g16>(L, x, batch, y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace aqlm

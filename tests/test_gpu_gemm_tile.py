@@ -1,13 +1,14 @@
-"""GPU parity of the 2x8 decoded-tile GEMM (gemm_tile.hip): the binding's gemm
-at 1536 or more activation rows on layers whose grid of 128-row x 256-row
-blocks gives every CU a block, i.e. the calls that run it.
+"""GPU parity of the decoded-tile GEMM (gemm_tile.hip) for the 2x8, 1x16 and
+1x16 g16 schemes: the binding's gemm at 512 or more activation rows on
+layers whose grid of 128-row x 256-row blocks has at least 160 blocks, i.e.
+the calls that run it.
 
 Checked against the oracle at the product tolerance and the tighter gate on
 sampled activation rows (first, last and seeded others): whole 128-row and
 256-row blocks, ragged rows and activation rows, rows not a multiple of four
 (the unpacked store path), the 11008x4096 MLP shape; one-hot activations
 return the decoded columns to within one float16 ulp; repeated calls give
-the same bits; nothing past y is written; codebooks large enough for the
+the same bits; nothing past y is written; 2x8 codebooks large enough for the
 float16 codeword sum to overflow take the halved table.
 """
 import numpy as np
@@ -21,10 +22,13 @@ from test_gpu_overflow import _large_layer
 
 pytestmark = pytest.mark.gpu
 
-# (out, in, batch): blocks of 128 rows x 256 activation rows, at least 256
+SCHEMES = {"2x8": WL.S2x8, "1x16": WL.S1x16, "1x16g16": WL.S1x16g16}
+
+# (out, in, batch): blocks of 128 rows x 256 activation rows, at least 160
 CASES = [(4096, 512, 2048),    # 32 x 8 whole blocks
          (4100, 1024, 1800),   # 33 x 8: a 4-row last row block, an 8-row last token block
          (4098, 512, 2000),    # rows not a multiple of 4: unpacked stores
+         (11008, 1024, 600),   # 86 x 3 from 600 rows: an 88-row last token block
          (11008, 4096, 2048)]  # the MLP shape
 
 
@@ -33,23 +37,26 @@ def _tokens(batch, n=64, seed=1):
     return np.unique(np.concatenate([[0, batch - 1], rng.choice(batch, n - 2, replace=False)]))
 
 
+@pytest.mark.parametrize("scheme", list(SCHEMES))
 @pytest.mark.parametrize("out,n_in,batch", CASES)
-def test_tile_gemm_matches_oracle(out, n_in, batch):
-    codes, books, scales, x = WL.small_case(out, n_in, WL.S2x8, batch, seed=out + n_in + batch)
+def test_tile_gemm_matches_oracle(out, n_in, batch, scheme):
+    codes, books, scales, x = WL.small_case(out, n_in, SCHEMES[scheme], batch,
+                                            seed=out + n_in + batch)
     L = dev_layer(codes, books, scales)
     toks = _tokens(batch)
     y_ref, bound = oracle.forward(x[toks], codes, books, scales)
     for ws in (True, False):
         y = L.gemm(dev_x(x), workspace=ws).cpu().numpy()
-        assert_product(y[toks], y_ref, bound, f"tile gemm {out}x{n_in} b{batch} ws={ws}")
+        assert_product(y[toks], y_ref, bound, f"tile gemm {scheme} {out}x{n_in} b{batch} ws={ws}")
 
 
-def test_tile_gemm_one_hot():
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_tile_gemm_one_hot(scheme):
     """Activation row i is e_(c_i): row i of y is column c_i of W, to within one
-    float16 ulp (the tile multiplies the float16 codeword sum and scales the
-    float32 total; one nonzero product per output)."""
+    float16 ulp (the tile multiplies the float16 codeword or codeword sum and
+    scales the float32 total; one nonzero product per output)."""
     out, n_in, batch = 4096, 512, 2048
-    codes, books, scales, _ = WL.small_case(out, n_in, WL.S2x8, 1, seed=21)
+    codes, books, scales, _ = WL.small_case(out, n_in, SCHEMES[scheme], 1, seed=21)
     L = dev_layer(codes, books, scales)
     w_ref = oracle.decode(codes, books, scales).astype(np.float32)
     cols = (np.arange(batch) * 37 + 5) % n_in
@@ -63,9 +70,10 @@ def test_tile_gemm_one_hot():
     assert bad.size == 0, bad[:8]
 
 
-def test_tile_gemm_deterministic_and_in_bounds():
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_tile_gemm_deterministic_and_in_bounds(scheme):
     out, n_in, batch = 4100, 512, 1800
-    codes, books, scales, x = WL.small_case(out, n_in, WL.S2x8, batch, seed=33)
+    codes, books, scales, x = WL.small_case(out, n_in, SCHEMES[scheme], batch, seed=33)
     L = dev_layer(codes, books, scales)
     canary = np.float16(-12345.0)
     ybuf = torch.full((batch * out + 64,), float(canary), dtype=torch.float16, device=device())
