@@ -100,6 +100,9 @@ def _parse():
                    help="llama2_7b_2x8 (default: the headline step), or per-layer tables for "
                         "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, "
                         "general_schemes, dequant, or the toy encoder's kernels: encode")
+    p.add_argument("--batches", default="",
+                   help="comma-separated activation-row counts for a per-layer table in place of "
+                        "the workload's own (e.g. 512,1024,2048 for gemm_mlp)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device-to-device copies of MIB MiB (for scaling the HBM "
                         "byte counters of a profiler) and exit")
@@ -265,7 +268,8 @@ def per_layer_tables(args):
         books = torch.from_numpy(d.codebooks).to(dev)
         scales = torch.from_numpy(d.scales).to(dev)
         kw = {"in_features": layer.in_features} if layer.packed else {}
-        batches = (1,) if name == "dequant" else wl.batches
+        batches = (1,) if name == "dequant" else (
+            tuple(int(v) for v in args.batches.split(",")) if args.batches else wl.batches)
         for batch in batches:
             b = WL.workload_bytes(layer, batch)
             copies = max(2, min(64, -(-ROTATE_BYTES // b["codes"])))
