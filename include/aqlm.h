@@ -141,7 +141,11 @@ AQLM_API int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch
  * ("AQLM (additive / multi-codebook quantization)", notes: dequantize to
  * float16, then a float16 matrix-engine product). x is [batch][in], y is
  * [batch][out], both float16. Up to 8 rows the call runs aqlm_gemv's
- * routes (the fastest form there) and gives its bits.
+ * routes (the fastest form there) and gives its bits. From 512 rows, for the
+ * three dedicated schemes with in a multiple of 64, where blocks of 128
+ * output rows x 256 activation rows number at least 160, each 128 x 64 weight
+ * tile is decoded once into on-chip memory and shared by all 256 activation
+ * rows of its block.
  */
 AQLM_API int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
               uint16_t *y, void *stream);
