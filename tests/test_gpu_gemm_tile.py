@@ -5,7 +5,8 @@ the calls that run it.
 
 Checked against the oracle at the product tolerance and the tighter gate on
 sampled activation rows (first, last and seeded others): whole 128-row and
-256-row blocks, ragged rows and activation rows, rows not a multiple of four
+256-row blocks, ragged rows and activation rows, 1, 3 and 5 K blocks (the
+tails of the unrolled K loops), rows not a multiple of four
 (the unpacked store path), the 11008x4096 MLP shape; one-hot activations
 return the decoded columns to within one float16 ulp; repeated calls give
 the same bits; nothing past y is written; 2x8 codebooks large enough for the
@@ -48,6 +49,21 @@ def test_tile_gemm_matches_oracle(out, n_in, batch, scheme):
     for ws in (True, False):
         y = L.gemm(dev_x(x), workspace=ws).cpu().numpy()
         assert_product(y[toks], y_ref, bound, f"tile gemm {scheme} {out}x{n_in} b{batch} ws={ws}")
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("n_in", [64, 192, 320])
+def test_tile_gemm_short_k(scheme, n_in):
+    """1, 3 and 5 K blocks of 64 inputs: the K loops' tails (the fill loop is
+    unrolled by four, the multiply loop by two) and a K loop that is only its
+    prologue. 2560 rows x 2048 activation rows: 20 x 8 = 160 blocks."""
+    out, batch = 2560, 2048
+    codes, books, scales, x = WL.small_case(out, n_in, SCHEMES[scheme], batch, seed=n_in + 7)
+    L = dev_layer(codes, books, scales)
+    toks = _tokens(batch)
+    y_ref, bound = oracle.forward(x[toks], codes, books, scales)
+    y = L.gemm(dev_x(x), workspace=False).cpu().numpy()
+    assert_product(y[toks], y_ref, bound, f"tile gemm {scheme} {out}x{n_in} b{batch}")
 
 
 @pytest.mark.parametrize("scheme", list(SCHEMES))
