@@ -96,6 +96,9 @@ def _parse():
                         "figure (0: two replays, for profiler runs)")
     p.add_argument("--no-context", action="store_true",
                    help="skip the ceilings and the dense float16 comparator")
+    p.add_argument("--cold-codebooks", action="store_true",
+                   help="also time each scheme's step with a copy of every layer's codebooks "
+                        "per block (codebooks read cold, like the codes): a secondary figure")
     p.add_argument("--workload", default=WORKLOAD,
                    help="llama2_7b_2x8 (default: the headline step), or per-layer tables for "
                         "single_2x8_512x1024, llama2_7b_1x16, llama2_70b_1x16, gemm_mlp, "
@@ -397,18 +400,26 @@ def scheme_step(torch, name, args, layers_np):
     base = [(torch.from_numpy(d.codes.view("int16") if d.codes.dtype.name == "uint16" else d.codes)
              .to(dev), torch.from_numpy(d.codebooks).to(dev), torch.from_numpy(d.scales).to(dev),
              torch.from_numpy(x).to(dev)) for (_, d, x, _) in layers_np]
-    blocks = []
-    for _ in range(MODEL_BLOCKS):
-        row = {}
-        for (layer, _, _, _), (codes, books, scales, x) in zip(layers_np, base):
-            L = AqlmLayer(codes.clone(), books, scales.clone())
-            row[layer.name] = [L, x.clone(), torch.empty((1, L.out_features), dtype=torch.float16,
-                                                         device=dev)]
-        # q, k and v share one input, as do gate and up
-        for a, b in (("k", "q"), ("v", "q"), ("up", "gate")):
-            row[a][1] = row[b][1]
-        blocks.append(row)
-    torch.cuda.synchronize()
+    def make_blocks(cold_books):
+        """MODEL_BLOCKS copies of the block's layers, each with codes, scales, x
+        and y of its own; the codebooks are shared (warm, the primary figure)
+        or, with cold_books, copied per block as well."""
+        out = []
+        for _ in range(MODEL_BLOCKS):
+            row = {}
+            for (layer, _, _, _), (codes, books, scales, x) in zip(layers_np, base):
+                L = AqlmLayer(codes.clone(), books.clone() if cold_books else books,
+                              scales.clone())
+                row[layer.name] = [L, x.clone(), torch.empty((1, L.out_features),
+                                                             dtype=torch.float16, device=dev)]
+            # q, k and v share one input, as do gate and up
+            for a, b in (("k", "q"), ("v", "q"), ("up", "gate")):
+                row[a][1] = row[b][1]
+            out.append(row)
+        torch.cuda.synchronize()
+        return out
+
+    blocks = make_blocks(False)
     nbytes = {l.name: nb for (l, _, _, nb) in layers_np}
     in2 = {l.name: 2 * l.in_features for (l, _, _, _) in layers_np}
 
@@ -423,12 +434,12 @@ def scheme_step(torch, name, args, layers_np):
             gemv_batched([row[m][0] for m in members], [row[m][1] for m in members],
                          [row[m][2] for m in members])
 
-    def step():
-        for row in blocks:
+    def step(rows):
+        for row in rows:
             for _, members in CALLS:
                 issue(row, members)
 
-    step_graph = _capture(torch, step)
+    step_graph = _capture(torch, lambda: step(blocks))
     for _ in range(args.warmup):
         step_graph.replay()
     torch.cuda.synchronize()
@@ -457,6 +468,16 @@ def scheme_step(torch, name, args, layers_np):
     achieved = (dom_bytes / dom_launches) / (avg_us * 1e-6) / 1e9
     layer_gbps = {n: nbytes[n] / us_layer[n] / 1e3 for n in idx}
     one_call_bytes = sum(nbytes.values())
+    # secondary, on request: every block with codebooks of its own, cold like
+    # its codes
+    book_bytes = sum(int(base[i][1].numel()) * 2 for i in range(len(base)))
+    cold_ms = None
+    if args.cold_codebooks:
+        cold = make_blocks(True)
+        cold_graph = _capture(torch, lambda: step(cold))
+        cold_ms = _graph_ms(torch, cold_graph)
+        del cold, cold_graph
+        torch.cuda.empty_cache()
     res = {
         "workload": spec["workload"],
         "scheme": spec["scheme"],
@@ -472,6 +493,13 @@ def scheme_step(torch, name, args, layers_np):
         "pct_of_peak_per_layer": {k: round(100 * v / HBM_PEAK_GBPS, 1) for k, v in layer_gbps.items()},
         "block_as_one_call_us": round(one_call_us, 3),
         "block_as_one_call_gbps": round(one_call_bytes / one_call_us / 1e3, 1),
+        "cold_codebooks": None if cold_ms is None else {
+            "block_step_us": round(1e3 * cold_ms / MODEL_BLOCKS, 3),
+            "gbps": round(step_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "codebook_bytes_per_block": book_bytes,
+            "note": "secondary: the same step with a copy of each layer's codebooks per block "
+                    "(read cold, like the codes); gbps counts codes + x + y only",
+        },
         "roofline": {
             "bound": "hbm",
             "kernel": spec["kernel"],
