@@ -8,7 +8,11 @@
 //                        codes once can reach);
 //   aqlm_ceiling_gather  random 16-byte loads from a table (the rate at which
 //                        a kernel can fetch codewords through the cache
-//                        hierarchy, one codeword per lane).
+//                        hierarchy, one codeword per lane);
+//   aqlm_ceiling_write   writes `bytes` of a buffer once with 16-byte
+//                        non-temporal stores (the pure-write ceiling that
+//                        the dequant kernel, which writes the dense float16
+//                        W, is judged against).
 //
 // Every load feeds a value that a (practically never taken) store to `sink`
 // depends on, so nothing is optimised away.
@@ -80,6 +84,23 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint4 *__restric
   fold_to_sink(acc, sink);
 }
 
+// Block b writes vectors [b * 256 * U, (b + 1) * 256 * U) of the buffer, U
+// coalesced 16-byte non-temporal stores per thread (the stores of the
+// dequant kernel).
+template <int U>
+__global__ __launch_bounds__(kThreads) void write_kernel(uint4 *__restrict__ buf, int64_t n16,
+                                                         uint32_t seed) {
+  const int64_t base = (int64_t)blockIdx.x * kThreads * U + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n16) {
+      const u32x4 v = {seed ^ (uint32_t)i, seed + (uint32_t)i, (uint32_t)(i >> 32), ~seed};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(buf) + i);
+    }
+  }
+}
+
 int cus() {
   int dev = 0, n = 256;
   if (hipGetDevice(&dev) == hipSuccess)
@@ -124,5 +145,27 @@ CEIL_API int aqlm_ceiling_gather(const void *table, int log2_entries, int per_la
   hipLaunchKernelGGL(gather_kernel, dim3(8 * cus()), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4 *>(table),
                      log2_entries, per_lane, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Write `bytes` (a multiple of 16) of buf once, per_thread (1, 2, 4 or 8)
+// stores of 16 bytes per thread, ceil(bytes / (4096 * per_thread)) blocks.
+// 0 on success.
+CEIL_API int aqlm_ceiling_write(void *buf, int64_t bytes, int per_thread, void *stream) {
+  if (!buf || bytes <= 0 || bytes % 16) return 1;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = (n16 + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
+  if (blocks >= ((int64_t)1 << 31)) return 1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint4 *b = static_cast<uint4 *>(buf);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  const uint32_t seed = 0x2545F491u;
+  switch (per_thread) {
+    case 1: hipLaunchKernelGGL(write_kernel<1>, grid, block, 0, st, b, n16, seed); break;
+    case 2: hipLaunchKernelGGL(write_kernel<2>, grid, block, 0, st, b, n16, seed); break;
+    case 4: hipLaunchKernelGGL(write_kernel<4>, grid, block, 0, st, b, n16, seed); break;
+    case 8: hipLaunchKernelGGL(write_kernel<8>, grid, block, 0, st, b, n16, seed); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -297,6 +297,12 @@ def per_layer_tables(args):
                    "us": round(us, 3),
                    "hbm_gbps": round(nbytes / us / 1e3, 1),
                    "pct_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBPS, 2)}
+            if op == "dequant" and not args.no_context:
+                wbytes = 2 * layer.out_features * layer.in_features
+                wc = write_ceiling_us(torch, w, wbytes, copies, reps)
+                row["write_ceiling_us"] = round(wc, 3)
+                row["write_ceiling_gbps"] = round(wbytes / wc / 1e3, 1)
+                row["pct_of_write_ceiling"] = round(100 * wc / us, 1)
             if op == "gemm":
                 flops = 2 * batch * layer.out_features * layer.in_features
                 row["tflops"] = round(flops / us / 1e6, 2)
@@ -527,7 +533,28 @@ def _ceiling_lib():
                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.aqlm_ceiling_gather.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.aqlm_ceiling_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_void_p]
     return lib
+
+
+def write_ceiling_us(torch, buf, nbytes, copies, reps):
+    """Pure-write time of nbytes into buf (16-byte non-temporal stores, the
+    dequant kernel's), launched `copies` times back to back in a HIP graph as
+    the dequant rows are: the fastest of 1, 2, 4 and 8 stores per thread."""
+    lib = _ceiling_lib()
+    best = None
+    for pt in (1, 2, 4, 8):
+        def fn(pt=pt):
+            for _ in range(copies):
+                if lib.aqlm_ceiling_write(buf.data_ptr(), nbytes, pt,
+                                          torch.cuda.current_stream().cuda_stream) != 0:
+                    raise RuntimeError("aqlm_ceiling_write failed")
+        g = _capture(torch, fn)
+        us = 1e3 * _time_graph(torch, g, reps) / copies
+        best = us if best is None else min(best, us)
+        del g
+    return best
 
 
 def ceilings(torch, sizes):
