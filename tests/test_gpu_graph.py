@@ -2,8 +2,8 @@
 benchmark times them) give on every replay exactly the bits of the same calls
 issued eagerly: GEMV (single and grouped), the GEMM with and without its
 workspace (split-K included, the workspace coming from the graph's memory
-pool; the one-tile form reading x in place, through the GEMV and the GEMM),
-and dequant. Eager work runs between the replays, and every replay is
+pool; the one-tile form reading x in place, through the GEMV and the GEMM;
+the decoded-tile kernel at 2048 rows, for 2x8 and 1x16 g16), and dequant. Eager work runs between the replays, and every replay is
 checked. Nothing here clears memory with a memset node: the kernels write
 every output element and the workspace form rewrites its workspace each call.
 """
@@ -27,6 +27,12 @@ def _calls():
     third = dev_layer(c3, b3, sc3)
     c5, b5, sc5, x5 = WL.small_case(7000, 2048, WL.S1x16g16, 16, seed=6)
     in_place = dev_layer(c5, b5, sc5)                              # one tile, x read in place
+    # the decoded-tile kernel: 20 x 8 = 160 blocks of 128 rows x 256 activation rows
+    c6, b6, sc6, x6 = WL.small_case(2560, 128, s2, 2048, seed=7)
+    tile_2x8 = dev_layer(c6, b6, sc6)
+    c7, b7, sc7, _ = WL.small_case(2560, 128, s16, 1, seed=8)
+    tile_g16 = dev_layer(c7, b7, sc7)
+    xt = dev_x(x6)
     xb, xs, x16 = dev_x(x), dev_x(x2), dev_x(x5)
     x4 = dev_x(x2[:4])
     assert in_place.workspace_bytes(16) == 0
@@ -41,6 +47,8 @@ def _calls():
         "dequant": torch.empty((300, 2048), dtype=torch.float16, device=device()),
         "gemv_in_place": torch.empty((4, 7000), dtype=torch.float16, device=device()),
         "gemm_in_place": torch.empty((16, 7000), dtype=torch.float16, device=device()),
+        "gemm_tile_2x8": torch.empty((2048, 2560), dtype=torch.float16, device=device()),
+        "gemm_tile_g16": torch.empty((2048, 2560), dtype=torch.float16, device=device()),
     }
 
     def run():
@@ -52,6 +60,8 @@ def _calls():
         small.dequant(out=outs["dequant"])
         in_place.gemv(x16[:4], out=outs["gemv_in_place"])
         in_place.gemm(x16, out=outs["gemm_in_place"])
+        tile_2x8.gemm(xt, out=outs["gemm_tile_2x8"])
+        tile_g16.gemm(xt, out=outs["gemm_tile_g16"], workspace=False)
 
     return run, outs, big, xb
 
