@@ -17,11 +17,10 @@
 //     chunk is the fp16 sum of the two codewords read from an 8 KiB LDS copy
 //     of the codebooks, as in every 2x8 matrix-core tile; a 1x16 chunk is the
 //     codeword (g 8) or half of it (g 16), gathered from the L2-resident
-//     codebook two K blocks ahead. Codes are loaded four K blocks ahead,
-//     activations four (1x16) or two (2x8) K blocks ahead, all with
-//     unconditional buffer loads (out of range offsets read zero: rows past
-//     the end decode to codeword 0 or codeword sums that are never stored,
-//     activation rows past the end are zero);
+//     codebook two K blocks ahead. Codes and activations are loaded four K
+//     blocks ahead, all with unconditional buffer loads (out of range
+//     offsets read zero: rows past the end decode to codeword 0 or codeword
+//     sums that are never stored, activation rows past the end are zero);
 //   * four multiplying wavefronts, one per SIMD next to a filling one: wave
 //     w multiplies all 128 rows with activation rows 64 w .. 64 w + 63,
 //     4 x 2 tiles of v_mfma_f32_32x32x16_f16 per 16-input step, both
