@@ -67,6 +67,21 @@ def test_tile_gemm_short_k(scheme, n_in):
 
 
 @pytest.mark.parametrize("scheme", list(SCHEMES))
+@pytest.mark.parametrize("out,n_in,batch", [(11008, 256, 511),   # wide tiles: below 512 rows
+                                            (11008, 256, 512),   # decoded tile: 86 x 2 = 172 blocks
+                                            (2560, 64, 4096)])   # 20 x 16 blocks, grid y 16
+def test_tile_gemm_routing_edges(scheme, out, n_in, batch):
+    """Both sides of the 512-row routing edge, and 4096 activation rows."""
+    codes, books, scales, x = WL.small_case(out, n_in, SCHEMES[scheme], batch, seed=batch + 3)
+    L = dev_layer(codes, books, scales)
+    toks = _tokens(batch)
+    y_ref, bound = oracle.forward(x[toks], codes, books, scales)
+    for ws in (True, False):
+        y = L.gemm(dev_x(x), workspace=ws).cpu().numpy()
+        assert_product(y[toks], y_ref, bound, f"gemm {scheme} {out}x{n_in} b{batch} ws={ws}")
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
 def test_tile_gemm_one_hot(scheme):
     """Activation row i is e_(c_i): row i of y is column c_i of W, to within one
     float16 ulp (the tile multiplies the float16 codeword or codeword sum and
