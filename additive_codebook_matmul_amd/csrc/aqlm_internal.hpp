@@ -52,10 +52,12 @@ int64_t gemm_ws_bytes(const LayerDesc &L, int64_t batch);
 bool gemm_mid_direct(const LayerDesc &L, int64_t batch);
 hipError_t launch_gemm_ws(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                           void *ws, hipStream_t stream);
-// 2x8 product for many activation rows with the weight tile decoded once into
-// LDS per 256 activation rows (gemm_tile.hip): whether it serves the layer at
-// this batch, and its launch.
+// Product for many activation rows with the weight tile decoded once into LDS
+// per 256 activation rows (gemm_tile.hip, the three dedicated schemes):
+// whether it serves the layer at this batch, its modelled duration (us),
+// whether aqlm_gemm takes it over the wide tiles, and its launch.
 bool gemm_tile_fits(const LayerDesc &L, int64_t batch);
+double gemm_tile_cost_us(const LayerDesc &L, int64_t batch);
 bool gemm_tile_preferred(const LayerDesc &L, int64_t batch);
 hipError_t launch_gemm_tile(const LayerDesc &L, const uint16_t *x, int64_t batch, uint16_t *y,
                             hipStream_t stream);

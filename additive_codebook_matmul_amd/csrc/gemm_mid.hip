@@ -499,16 +499,31 @@ int mid_nt(int64_t batch) {
   return n <= 4 ? n : n <= 6 ? 6 : 8;
 }
 
-// Above 128 rows the wide tiles (256 output rows x 64 or 128 activation
-// rows per workgroup, no split of K) take over once their grid gives most
-// CUs a workgroup (measured on 11008 x 4096 and 4096 x 11008 layers, 129 to
-// 2048 rows); below that the 128-row blocks of this kernel, with K split as
-// needed, keep every CU busy.
-bool mid_beats_wide(const LayerDesc &L, int64_t batch) {
-  const int64_t wide_rows = L.scheme == Scheme::k2x8 ? 64 : 128;
-  const int64_t wide_blocks = ((L.out + 255) / 256) * ((batch + wide_rows - 1) / wide_rows);
-  return wide_blocks < kMidCus * 5 / 8;
+// Above 128 rows this form (blocks of 128 activation rows) takes every call
+// it can plan, up to 4096 rows, except
+//   * where aqlm_gemm would run the decoded-tile kernel (gemm_tile.hip) and
+//     that kernel's timing model is below this form's: the clock model of
+//     mid_plan times mid_us_per_unit, the mean ratio of measured kernel times
+//     to the model on 11008x4096 and 4096x11008 layers at 129..2048 rows
+//     (within 20 % at every point);
+//   * where the workspace would pass 64 MiB, the static scratch of
+//     aqlm_gemm_noalloc: such calls keep a route that needs none.
+// Those calls run as aqlm_gemm. Measured times on those layers (us):
+//                        rows   this form   tile kernel   wide tiles
+//   2x8      11008x4096   384       57          77            91
+//                         640       93         141           104
+//                        2048      286         269           331
+//            4096x11008   640       98         164           136
+//                        1536      175         196           235
+//   1x16 g16 11008x4096   448      122          84           123
+//            4096x11008   512      106         202           314
+//   1x16     4096x11008   256       82         187           284
+//                        1024      268         229           350
+// The wide tiles are slower than one of the other two at nearly every size.
+double mid_us_per_unit(Scheme s) {
+  return s == Scheme::k2x8 ? 1.15e-3 : s == Scheme::k1x16g16 ? 0.53e-3 : 0.72e-3;
 }
+constexpr size_t kMidMaxWsAbove128 = size_t(64) << 20;
 
 bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
   // (bit-packed 8- and 16-bit codes are the element layout's bytes)
@@ -519,7 +534,6 @@ bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
   // above 128 rows: blocks of 128 activation rows, one more grid dimension
   const int nt = batch <= 128 ? mid_nt(batch) : 8;
   const int ntb = (int)((batch + 16 * nt - 1) / (16 * nt));
-  if (batch > 128 && !mid_beats_wide(L, batch)) return false;
   const int64_t bp = 16 * nt * ntb;
   const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
   const int64_t nsc = (L.groups + kGroupsPerSc - 1) / kGroupsPerSc;
@@ -565,6 +579,13 @@ bool mid_plan(const LayerDesc &L, int64_t batch, MidPlan *p) {
   p->part_off = align256((size_t)xb_bytes);
   p->total = p->part_off +
              (p->splits > 1 ? (size_t)p->nrb * p->splits * p->ntb * p->rt * p->nt * 1024 : 0);
+  if (batch > 128) {
+    if (p->total > kMidMaxWsAbove128) return false;
+    // the call then runs as aqlm_gemm, which takes the decoded-tile kernel
+    if (gemm_tile_preferred(L, batch) &&
+        gemm_tile_cost_us(L, batch) < best * mid_us_per_unit(L.scheme))
+      return false;
+  }
   return p->total < (size_t(1) << 40);
 }
 

@@ -45,6 +45,7 @@
 // reads pinned two steps ahead of their MFMAs (no gain), the 2x8 codebooks
 // in a 64 KiB bank-spread table (conflict-free decode reads; no gain), one
 // role for all 256 threads of a four-wavefront block (301 us).
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -378,21 +379,37 @@ bool gemm_tile_fits(const LayerDesc &L, int64_t batch) {
          (batch + kTBN) * L.in * 2 + 4096 < (int64_t(1) << 31);
 }
 
-// Where it runs instead of the wide tiles: from 512 activation rows, when
-// its grid has at least 160 blocks. Same-box timings of the binding's gemm
-// (wide tiles -> this kernel, us):
-//                        512 rows      1024 rows     2048 rows
-//   2x8      11008x4096  99 -> 79      169 -> 158    301 -> 261..276
-//            4096x11008  61 -> 60      162 -> 173    260 -> 230..240
-//   1x16 g16 11008x4096  126 -> 86     254 -> 173    410 -> 298..312
-//            4096x11008  113 -> 112    214 -> 218    389 -> 274..289
-//   1x16     11008x4096  175 -> 105    345 -> 217    581 -> 370..380
-//            4096x11008  146 -> 141    272 -> 269    505 -> 343..354
-// (4096x11008 has 64 blocks at 512 rows and 128 at 1024); at 256 rows on
-// 11008x4096 (86 blocks) the 2x8 tile was slower (67 -> 84 us).
+// Modelled duration in microseconds. One block per CU, so the grid runs in
+// rounds of up to 256 blocks; a round costs a + b * (its blocks / 256) per K
+// block of 64 inputs (the b term: HBM and L2 contention as the round fills).
+// a and b per scheme are fitted to kernel times on 11008x4096 and 4096x11008
+// layers from 129 to 2048 rows (one round of 32..256 blocks, and two or
+// three rounds), which the model follows to within 10 %.
+double gemm_tile_cost_us(const LayerDesc &L, int64_t batch) {
+  const double a = L.scheme == Scheme::k2x8 ? 0.83 : L.scheme == Scheme::k1x16g16 ? 0.83 : 0.93;
+  const double b = L.scheme == Scheme::k2x8 ? 0.51 : L.scheme == Scheme::k1x16g16 ? 0.85 : 1.05;
+  int64_t blocks = ((L.out + kTBM - 1) / kTBM) * ((batch + kTBN - 1) / kTBN);
+  double per_kb = 0.0;
+  while (blocks > 0) {
+    const int64_t round = std::min<int64_t>(blocks, 256);
+    per_kb += a + b * (double)round / 256.0;
+    blocks -= round;
+  }
+  return per_kb * (double)(L.in / kTKIn);
+}
+
+// The route of aqlm_gemm (no workspace) above 128 rows, against the wide
+// tiles. 1x16 and 1x16 g16: wherever the kernel fits; the codeword gathers
+// of the wide tiles cost more at every size measured (11008x4096 and
+// 4096x11008, 129..2048 rows: 1.0-1.6x this kernel's time, 1.5-2.4x on the
+// 4096-row layer). 2x8: from 512 rows when the grid has at least 160 blocks;
+// below that the wide tiles' 64-row blocks keep more CUs busy (11008x4096 at
+// 129..320 rows: wide 63-69 us, this kernel 68-76 us; 4096x11008 is faster
+// in the wide tiles up to 1024 rows: 123-156 us against 154-174 us).
 bool gemm_tile_preferred(const LayerDesc &L, int64_t batch) {
-  if (batch < 512 || !gemm_tile_fits(L, batch)) return false;
-  return ((L.out + kTBM - 1) / kTBM) * ((batch + kTBN - 1) / kTBN) >= 160;
+  if (batch <= 128 || !gemm_tile_fits(L, batch)) return false;
+  if (L.scheme != Scheme::k2x8) return true;
+  return batch >= 512 && ((L.out + kTBM - 1) / kTBM) * ((batch + kTBN - 1) / kTBN) >= 160;
 }
 
 namespace {

@@ -141,11 +141,12 @@ AQLM_API int aqlm_gemv(const aqlm_layer *layer, const uint16_t *x, int64_t batch
  * ("AQLM (additive / multi-codebook quantization)", notes: dequantize to
  * float16, then a float16 matrix-engine product). x is [batch][in], y is
  * [batch][out], both float16. Up to 8 rows the call runs aqlm_gemv's
- * routes (the fastest form there) and gives its bits. From 512 rows, for the
- * three dedicated schemes with in a multiple of 64, where blocks of 128
- * output rows x 256 activation rows number at least 160, each 128 x 64 weight
- * tile is decoded once into on-chip memory and shared by all 256 activation
- * rows of its block.
+ * routes (the fastest form there) and gives its bits. Above 128 rows, for the
+ * three dedicated schemes with in a multiple of 64 (1x16 and 1x16 g16 at any
+ * such batch; 2x8 from 512 rows where blocks of 128 output rows x 256
+ * activation rows number at least 160), each 128 x 64 weight tile is decoded
+ * once into on-chip memory and shared by all 256 activation rows of its
+ * block; other calls above 128 rows run tiles of 256 output rows.
  */
 AQLM_API int aqlm_gemm(const aqlm_layer *layer, const uint16_t *x, int64_t batch,
               uint16_t *y, void *stream);
@@ -163,10 +164,11 @@ AQLM_API int aqlm_gemm_workspace_size(const aqlm_layer *layer, int64_t batch, in
  * aqlm_gemm_ws: the product of aqlm_gemm with a caller-owned device
  * workspace, which lets the three dedicated schemes (2x8, 1x16 and 1x16 with
  * g = 16; element or bit-packed codes, in / g a multiple of 8) run the
- * workspace form of the matrix-core path from 17 rows up to the batch where
- * the wide tiles of aqlm_gemm fill the chip by themselves (at most 4096
- * rows). (At 1..16 rows, on layers whose row blocks fill half the chip
- * without splitting K, the same form reads x in place and needs no
+ * workspace form of the matrix-core path from 17 rows up to 128, and above
+ * that up to 4096 rows wherever the workspace stays within 64 MiB and, if
+ * aqlm_gemm would run its decoded-tile kernel, the library's timing model of
+ * the workspace form is below that kernel's. (At 1..16 rows, on layers whose row blocks fill half
+ * the chip without splitting K, the same form reads x in place and needs no
  * workspace; aqlm_gemm and aqlm_gemv run it there themselves.) From 17 rows
  * the activations are first re-laid into blocks of 8 inputs so that every
  * MFMA operand load is contiguous, rows beyond 128 go to blocks of 128, and

@@ -131,10 +131,11 @@ def _ws_size(s, batch):
 
 def test_workspace_size():
     """Host-side sizing: the workspace form covers the three dedicated schemes
-    (element or bit-packed codes) with in/g a multiple of 8 from 17 rows while
-    the wide tiles' grid is small, and then holds at least the re-laid
-    activations (in x 16*ceil(batch/16) float16 values); at 1..16 rows it
-    reads x in place and needs none."""
+    (element or bit-packed codes) with in/g a multiple of 8 from 17 rows to
+    128, and above that wherever its workspace stays within 64 MiB and its
+    timing model beats the decoded-tile kernel that aqlm_gemm would run; it
+    then holds at least the re-laid activations (in x 16*ceil(batch/16)
+    float16 values). At 1..16 rows it reads x in place and needs none."""
     mlp = dict(out=4096, n_in=11008)
     for M, B, g in ((2, 8, 8), (1, 16, 8), (1, 16, 16)):
         for batch in (17, 33, 64, 100, 128):
@@ -148,8 +149,13 @@ def test_workspace_size():
     assert _ws_size(_layer(out=11008, n_in=4096), 17)[1] > 0         # re-laid activations
     assert _ws_size(_layer(out=300, n_in=1024), 8) == (0, 0)         # few row blocks: skinny
     assert _ws_size(_layer(**mlp), 129)[1] > 0                       # two blocks of 128 rows
-    assert _ws_size(_layer(**mlp), 4096) == (0, 0)                   # the wide tiles fill the chip
-    assert _ws_size(_layer(out=11008, n_in=4096), 1024) == (0, 0)
+    assert _ws_size(_layer(**mlp), 1024)[1] >= 11008 * 1024 * 2      # 8 blocks of 128 rows
+    assert _ws_size(_layer(**mlp), 4096) == (0, 0)                   # would pass 64 MiB
+    up = dict(out=11008, n_in=4096)
+    assert _ws_size(_layer(**up), 1024)[1] >= 4096 * 1024 * 2        # modelled 141 us, tile 150
+    assert _ws_size(_layer(**up), 2048) == (0, 0)                    # modelled 259 us, tile 247
+    assert _ws_size(_layer(1, 16, 8, **up), 200) == (0, 0)           # 1x16: the tile kernel
+    assert _ws_size(_layer(1, 16, 8, **mlp), 200)[1] > 0             # 32 tiles: this form
     assert _ws_size(_layer(3, 8, 8, **mlp), 64) == (0, 0)            # general scheme
     assert _ws_size(_layer(flags=1, **mlp), 64) == _ws_size(_layer(**mlp), 64)  # same bytes
     assert _ws_size(_layer(3, 8, 8, flags=1, **mlp), 64) == (0, 0)   # general, bit-packed
@@ -176,8 +182,8 @@ def test_noalloc_rejects_calls_beyond_the_static_scratch():
     workspace form would need more than the static scratch array holds."""
     f = _lib.load_library().aqlm_gemm_noalloc
     big = None
-    for out, n_in in ((1024, 28672), (1024, 65536)):
-        for batch in (1000, 2000):
+    for out, n_in in ((1024, 1 << 18), (1024, 1 << 19)):
+        for batch in (100, 128):
             s = _layer(out=out, n_in=n_in)
             st, need = _ws_size(s, batch)
             if st == 0 and need > _lib.STATIC_SCRATCH_BYTES:

@@ -1,7 +1,9 @@
 """GPU parity of the decoded-tile GEMM (gemm_tile.hip) for the 2x8, 1x16 and
-1x16 g16 schemes: the binding's gemm at 512 or more activation rows on
-layers whose grid of 128-row x 256-row blocks has at least 160 blocks, i.e.
-the calls that run it.
+1x16 g16 schemes: the binding's gemm without workspace (aqlm_gemm) above 128
+activation rows for 1x16 and 1x16 g16, and for 2x8 from 512 rows on layers
+whose grid of 128-row x 256-row blocks has at least 160 blocks, i.e. the
+calls that run it (with a workspace, the calls whose timing model prefers it
+to the workspace form run it too).
 
 Checked against the oracle at the product tolerance and the tighter gate on
 sampled activation rows (first, last and seeded others): whole 128-row and
@@ -46,7 +48,7 @@ def test_tile_gemm_matches_oracle(out, n_in, batch, scheme):
     L = dev_layer(codes, books, scales)
     toks = _tokens(batch)
     y_ref, bound = oracle.forward(x[toks], codes, books, scales)
-    for ws in (True, False):
+    for ws in (True, False):  # without a workspace: the tile kernel
         y = L.gemm(dev_x(x), workspace=ws).cpu().numpy()
         assert_product(y[toks], y_ref, bound, f"tile gemm {scheme} {out}x{n_in} b{batch} ws={ws}")
 
@@ -67,11 +69,12 @@ def test_tile_gemm_short_k(scheme, n_in):
 
 
 @pytest.mark.parametrize("scheme", list(SCHEMES))
-@pytest.mark.parametrize("out,n_in,batch", [(11008, 256, 511),   # wide tiles: below 512 rows
+@pytest.mark.parametrize("out,n_in,batch", [(11008, 256, 511),   # 2x8: wide tiles below 512 rows
                                             (11008, 256, 512),   # decoded tile: 86 x 2 = 172 blocks
                                             (2560, 64, 4096)])   # 20 x 16 blocks, grid y 16
 def test_tile_gemm_routing_edges(scheme, out, n_in, batch):
-    """Both sides of the 512-row routing edge, and 4096 activation rows."""
+    """Both sides of the 2x8 512-row edge of aqlm_gemm, and 4096 activation
+    rows; with and without a workspace."""
     codes, books, scales, x = WL.small_case(out, n_in, SCHEMES[scheme], batch, seed=batch + 3)
     L = dev_layer(codes, books, scales)
     toks = _tokens(batch)
@@ -94,7 +97,7 @@ def test_tile_gemm_one_hot(scheme):
     cols[:4] = (0, 7, n_in - 8, n_in - 1)
     x = np.zeros((batch, n_in), dtype=np.float16)
     x[np.arange(batch), cols] = 1
-    y = L.gemm(dev_x(x)).cpu().numpy().astype(np.float32)
+    y = L.gemm(dev_x(x), workspace=False).cpu().numpy().astype(np.float32)
     ref = w_ref[:, cols].T
     ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float32)
     bad = np.argwhere(np.abs(y - ref) > ulp)
@@ -109,10 +112,10 @@ def test_tile_gemm_deterministic_and_in_bounds(scheme):
     canary = np.float16(-12345.0)
     ybuf = torch.full((batch * out + 64,), float(canary), dtype=torch.float16, device=device())
     y = ybuf[: batch * out].view(batch, out)
-    L.gemm(dev_x(x), out=y)
+    L.gemm(dev_x(x), out=y, workspace=False)
     first = bits(y)
     assert torch.all(ybuf[batch * out:] == float(canary))
-    L.gemm(dev_x(x), out=y)
+    L.gemm(dev_x(x), out=y, workspace=False)
     assert np.array_equal(first, bits(y))
 
 
@@ -121,7 +124,7 @@ def test_tile_gemm_large_codebooks():
     at s = 0.25 on every row: finite outputs within the product tolerance."""
     codes, books, scales, x, _ = _large_layer(4096, 512, 2048, seed=9)
     L = dev_layer(codes, books, scales)
-    y = L.gemm(dev_x(x)).cpu().numpy()
+    y = L.gemm(dev_x(x), workspace=False).cpu().numpy()
     assert np.isfinite(y.astype(np.float32)).all()
     toks = _tokens(2048)
     y_ref, bound = oracle.forward(x[toks], codes, books, scales)
