@@ -369,11 +369,12 @@ __global__ __launch_bounds__(kTThreads) void gemm_tile_kernel(
 }  // namespace
 
 // True when the decoded-tile kernel serves this layer and batch: a dedicated
-// scheme, whole K blocks (in a multiple of 64) and 32-bit byte offsets for the
-// codes (rows of one block past the end) and the activations (one block past
-// the end).
+// scheme (element or bit-packed codes: for 8- and 16-bit codes the packed
+// stream holds the element layout's bytes), whole K blocks (in a multiple of
+// 64) and 32-bit byte offsets for the codes (rows of one block past the end)
+// and the activations (one block past the end).
 bool gemm_tile_fits(const LayerDesc &L, int64_t batch) {
-  if (L.scheme == Scheme::kGeneral || L.packed || L.in % kTKIn != 0) return false;
+  if (L.scheme == Scheme::kGeneral || L.in % kTKIn != 0) return false;
   const int64_t row_bytes = L.groups * kCodeBytesPerGroup;
   return (L.out + kTBM) * row_bytes + 4096 < (int64_t(1) << 31) &&
          (batch + kTBN) * L.in * 2 + 4096 < (int64_t(1) << 31);
