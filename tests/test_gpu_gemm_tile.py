@@ -11,15 +11,16 @@ sampled activation rows (first, last and seeded others): whole 128-row and
 tails of the unrolled K loops), rows not a multiple of four
 (the unpacked store path), the 11008x4096 MLP shape; one-hot activations
 return the decoded columns to within one float16 ulp; repeated calls give
-the same bits; nothing past y is written; 2x8 codebooks large enough for the
-float16 codeword sum to overflow take the halved table.
+the same bits; nothing past y is written; bit-packed codes give the element
+layout's bits; 2x8 codebooks large enough for the float16 codeword sum to
+overflow take the halved table.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from additive_codebook_matmul_amd import workloads as WL
+from additive_codebook_matmul_amd import AqlmLayer, workloads as WL
 from gpu_util import assert_product, bits, dev_layer, dev_x, device
 from test_gpu_overflow import _large_layer
 
@@ -129,3 +130,19 @@ def test_tile_gemm_large_codebooks():
     toks = _tokens(2048)
     y_ref, bound = oracle.forward(x[toks], codes, books, scales)
     assert_product(y[toks], y_ref, bound, "tile gemm, large codebooks")
+
+
+@pytest.mark.parametrize("scheme", list(SCHEMES))
+def test_tile_gemm_bit_packed_codes(scheme):
+    """The bit-packed flag (8- and 16-bit codes: the stream holds the element
+    layout's bytes) takes the same tile kernel and gives the same bits.
+    2560 x 128 at 2048 rows: 20 x 8 = 160 blocks."""
+    s = SCHEMES[scheme]
+    out, n_in, batch = 2560, 128, 2048
+    codes, books, scales, x = WL.small_case(out, n_in, s, batch, seed=44)
+    plain = dev_layer(codes, books, scales)
+    packed = AqlmLayer(torch.from_numpy(WL.pack_codes(codes, s.B).view(np.int32)).to(device()),
+                       torch.from_numpy(books).to(device()), torch.from_numpy(scales).to(device()),
+                       in_features=n_in)
+    xd = dev_x(x)
+    assert np.array_equal(bits(packed.gemm(xd, workspace=False)), bits(plain.gemm(xd, workspace=False)))
