@@ -12,7 +12,14 @@
 //   aqlm_ceiling_write   writes `bytes` of a buffer once with 16-byte
 //                        non-temporal stores (the pure-write ceiling that
 //                        the dequant kernel, which writes the dense float16
-//                        W, is judged against).
+//                        W, is judged against);
+//   aqlm_ceiling_lds     LDS access rates of the patterns the kernels use:
+//                        conflict-free and four-address (broadcast) 16-byte
+//                        reads, random 8-byte reads from 128 KiB, random
+//                        16-byte reads from 8 KiB, conflict-free 16-byte
+//                        writes; with the shader clock read inside the
+//                        kernel (core-clock counter against the 100 MHz
+//                        real-time counter), so rates come out per clock.
 //
 // Every load feeds a value that a (practically never taken) store to `sink`
 // depends on, so nothing is optimised away.
@@ -24,6 +31,7 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 
 // One word per block: the XOR of every thread's value.
@@ -101,6 +109,84 @@ __global__ __launch_bounds__(kThreads) void write_kernel(uint4 *__restrict__ buf
   }
 }
 
+// LDS patterns. Every lane keeps 16 byte offsets in registers (a random
+// sample of its pattern, drawn by an LCG at the start) and cycles through
+// them; an empty asm statement marks each offset as changed before its use,
+// so the accesses stay in the loop, and a read feeds one three-operand add
+// per 8 bytes into the lane's fold (every byte of the read is used, so its
+// width is kept).
+//   0  16-byte reads, lane l at 16 l + 1024 k: the 16 lanes of every pass
+//      cover all 64 banks once (the GEMV's A-operand table reads);
+//   1  16-byte reads, four addresses per wavefront (lane / 16 picks one):
+//      the GEMV's activation fragments at one activation row;
+//   2  8-byte reads at random 8-byte entries of a 128 KiB table (the
+//      codebook-sliced 1x16 GEMV's lookups);
+//   3  16-byte reads at random 16-byte entries of an 8 KiB table (a 2x8
+//      codebook copy read by a decode);
+//   4  16-byte writes, lane l at 16 l + 1024 k (conflict-free).
+constexpr int kLdsOffsets = 16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+template <int MODE>
+__global__ __launch_bounds__(1024) void lds_kernel(int iters, uint32_t *__restrict__ sink,
+                                                  unsigned long long *__restrict__ clocks) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr uint32_t kBytes = MODE == 2 ? 131072u : MODE == 3 ? 8192u : 65536u;
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (uint32_t i = (uint32_t)tid * 16u; i < kBytes; i += 1024u * 16u)
+    *reinterpret_cast<u32x4 *>(lds + i) = u32x4{i, i ^ 0x55u, i + 7u, ~i};
+  const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t *)lds);
+  uint32_t off[kLdsOffsets];
+  uint32_t h = (blockIdx.x * 1024u + (uint32_t)tid) * 2654435761u + 977u;
+  const uint32_t wv = (uint32_t)(tid >> 6);
+#pragma unroll
+  for (int k = 0; k < kLdsOffsets; ++k) {
+    h = h * 1664525u + 1013904223u;
+    uint32_t o;
+    if (MODE == 0 || MODE == 4)
+      o = ((uint32_t)lane * 16u + ((uint32_t)k * 16u + wv) * 1024u) & (kBytes - 1u);
+    else if (MODE == 1)
+      o = ((uint32_t)(lane >> 4) * 16u + ((uint32_t)k * 16u + wv) * 64u) & (kBytes - 1u);
+    else if (MODE == 2)
+      o = ((h >> 9) & 16383u) * 8u;
+    else
+      o = ((h >> 9) & 511u) * 16u;
+    off[k] = base + o;
+  }
+  __syncthreads();
+  unsigned long long c0 = 0, r0 = 0;
+  if (tid == 0) {
+    c0 = clock64();
+    r0 = wall_clock64();
+  }
+  uint32_t acc = 0, acc2 = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < kLdsOffsets; ++k) {
+      uint32_t a = off[k];
+      asm volatile("" : "+v"(a));
+      if constexpr (MODE == 4) {
+        *reinterpret_cast<lds_u32x4 *>((uintptr_t)a) = u32x4{acc, acc2, 0u, 1u};
+        acc += 1u;
+      } else if constexpr (MODE == 2) {
+        const u32x2 v = *reinterpret_cast<const lds_u32x2 *>((uintptr_t)a);
+        acc = v.x + v.y + acc;
+      } else {
+        const u32x4 v = *reinterpret_cast<const lds_u32x4 *>((uintptr_t)a);
+        acc = v.x + v.y + acc;
+        acc2 = v.z + v.w + acc2;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    clocks[2 * blockIdx.x] = clock64() - c0;
+    clocks[2 * blockIdx.x + 1] = wall_clock64() - r0;
+  }
+  if ((acc ^ acc2) == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
 int cus() {
   int dev = 0, n = 256;
   if (hipGetDevice(&dev) == hipSuccess)
@@ -166,6 +252,42 @@ CEIL_API int aqlm_ceiling_write(void *buf, int64_t bytes, int per_thread, void *
     case 4: hipLaunchKernelGGL(write_kernel<4>, grid, block, 0, st, b, n16, seed); break;
     case 8: hipLaunchKernelGGL(write_kernel<8>, grid, block, 0, st, b, n16, seed); break;
     default: return 1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// Dynamic LDS bytes of an aqlm_ceiling_lds mode (0 .. 4), 0 for an unknown
+// mode.
+CEIL_API int aqlm_ceiling_lds_bytes(int mode) {
+  return mode == 2 ? 131072 : mode == 3 ? 8192 : (mode >= 0 && mode <= 4) ? 65536 : 0;
+}
+
+// LDS access rate of `mode` (see lds_kernel): `blocks` workgroups of 1024
+// threads (sixteen wavefronts; one per CU when `blocks` is the CU count),
+// each lane issuing 16 * iters accesses. clocks receives, per block, the core-clock cycles and
+// the 100 MHz real-time ticks between the block's first and last access
+// (2 * blocks words); sink must hold `blocks` words. 0 on success.
+CEIL_API int aqlm_ceiling_lds(int mode, int blocks, int iters, uint32_t *sink,
+                              unsigned long long *clocks, void *stream) {
+  const int bytes = aqlm_ceiling_lds_bytes(mode);
+  if (!bytes || blocks <= 0 || iters <= 0 || !sink || !clocks) return 1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)blocks), block(1024);
+  hipError_t e = hipSuccess;
+  switch (mode) {
+#define CEIL_LDS_CASE(M)                                                                         \
+  case M:                                                                                        \
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(lds_kernel<M>),                       \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);                  \
+    if (e != hipSuccess) return 2;                                                               \
+    hipLaunchKernelGGL(lds_kernel<M>, grid, block, bytes, st, iters, sink, clocks);              \
+    break;
+    CEIL_LDS_CASE(0)
+    CEIL_LDS_CASE(1)
+    CEIL_LDS_CASE(2)
+    CEIL_LDS_CASE(3)
+    CEIL_LDS_CASE(4)
+#undef CEIL_LDS_CASE
   }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -36,6 +36,7 @@
 #include "aqlm_device.hpp"
 
 #include <atomic>
+#include <type_traits>
 
 namespace aqlm {
 namespace {
@@ -191,23 +192,20 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
   }
   const float total_mul = halved ? 2.0f : 1.0f;
 
-  // B fragments do not depend on the tile: for blocks of three or more tiles
-  // with two chunks per wavefront (16 fragments, 64 registers) they are read
-  // from LDS once, before the first tile, and kept in registers (gate,up call
-  // 11.1 -> 10.9 us; with one or two tiles per block the up-front reads only
-  // delay the first tile: o 4.05 -> 4.2 us).
-  constexpr bool kHoldB = MAXC <= 2 && !ALL;
-  uint4 bh[kHoldB ? MAXC : 1][8];
-  if constexpr (kHoldB) {
-#pragma unroll
-    for (int k = 0; k < MAXC; ++k)
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        bh[k][s] = k < nw ? *reinterpret_cast<const uint4 *>(xrow + (k * 32 + s) * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
-  }
+  // B fragments do not depend on the tile. In the two-chunk class a
+  // wavefront's 16 fragments (64 registers) read by its first tile are kept
+  // for its later ones: a four-address 16-byte LDS read costs as much LDS
+  // time as a conflict-free one (about 4.3 clocks per wavefront), a third of
+  // a tile's LDS reads (q,k,v call, two tiles per block, 7.9 -> 7.7 us).
+  // Reading them all before the first tile instead delays that tile (o,
+  // one tile per block: 4.05 -> 4.2 us).
+  constexpr bool kKeepB = MAXC <= 2 && (!ALL || NBUF == 2);
+  uint4 bh[kKeepB ? MAXC : 1][8];
 
-  auto tile = [&](int i, const uint4 (&c)[MAXC]) {
+  // bmode 0: fragments read from LDS; 1: read from LDS and kept in bh;
+  // 2: taken from bh
+  auto tile = [&](int i, const uint4 (&c)[MAXC], auto bmode) {
+    constexpr int BM = decltype(bmode)::value;
     float4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < MAXC; ++k) {
@@ -223,10 +221,11 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
             const uint32_t addrB = __builtin_amdgcn_perm(w[s >> 1], baseB, selB[s & 1]);
             a0[u] = *reinterpret_cast<const uint4 *>(table + addrA);
             a1[u] = *reinterpret_cast<const uint4 *>(table + addrB);
-            if constexpr (kHoldB)
-              b[u] = bh[kHoldB ? k : 0][s];
+            if constexpr (BM == 2)
+              b[u] = bh[kKeepB ? k : 0][s];
             else
               b[u] = *reinterpret_cast<const uint4 *>(xrow + (k * 32 + s) * 8);
+            if constexpr (BM == 1) bh[kKeepB ? k : 0][s] = b[u];
           }
           // two accumulators so that consecutive MFMAs are independent
 #pragma unroll
@@ -262,20 +261,32 @@ __device__ __forceinline__ void gemv_2x8_mfma_body(const MfmaLayer &L, int blk) 
     }
   };
 
+  using keep_first = std::integral_constant<int, kKeepB ? 1 : 0>;
+  using keep_rest = std::integral_constant<int, kKeepB ? 2 : 0>;
   if constexpr (ALL) {
     // my_tiles <= NBUF: every tile was loaded in the prologue
+    if (my_tiles > 0) tile(0, cw[0], keep_first{});
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u)
-      if (u < my_tiles) tile(u, cw[u]);
-  } else {
+    for (int u = 1; u < NBUF; ++u)
+      if (u < my_tiles) tile(u, cw[u], keep_rest{});
+  } else if (my_tiles > 0) {
     // NBUF tiles per loop pass so that every code buffer index is static;
     // each buffer is refilled with the codes NBUF tiles ahead right after its
-    // tile
-    for (int i0 = 0; i0 < my_tiles; i0 += NBUF) {
+    // tile (the first pass is peeled off: its first tile keeps the fragments)
+    tile(0, cw[0], keep_first{});
+    load_tile(NBUF, cw[0]);
+#pragma unroll
+    for (int u = 1; u < NBUF; ++u) {
+      if (u < my_tiles) {
+        tile(u, cw[u], keep_rest{});
+        load_tile(u + NBUF, cw[u]);
+      }
+    }
+    for (int i0 = NBUF; i0 < my_tiles; i0 += NBUF) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         if (i0 + u < my_tiles) {
-          tile(i0 + u, cw[u]);
+          tile(i0 + u, cw[u], keep_rest{});
           load_tile(i0 + u + NBUF, cw[u]);
         }
       }

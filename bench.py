@@ -259,9 +259,15 @@ def per_layer_tables(args):
     load_library()
     dev = torch.device("cuda:0")
     name = args.workload
-    wl = WL.WORKLOADS["llama2_7b_2x8" if name == "dequant" else name]
+    if name == "dequant":
+        # the 7B layer sets of both schemes and the 1x16 g16 MLP layers
+        layers = (WL.WORKLOADS["llama2_7b_2x8"].layers + WL.WORKLOADS["llama2_7b_1x16"].layers
+                  + tuple(l for l in WL.WORKLOADS["gemm_mlp"].layers if l.scheme == WL.S1x16g16))
+    else:
+        layers = WL.WORKLOADS[name].layers
+        wl = WL.WORKLOADS[name]
     rows = []
-    for layer in wl.layers:
+    for layer in layers:
         d = WL.make_layer(layer)
         if layer.packed:
             codes = torch.from_numpy(WL.pack_codes(d.codes, layer.scheme.B).view("int32")).to(dev)
@@ -535,7 +541,59 @@ def _ceiling_lib():
                                         ctypes.c_void_p, ctypes.c_void_p]
     lib.aqlm_ceiling_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                        ctypes.c_void_p]
+    lib.aqlm_ceiling_lds_bytes.argtypes = [ctypes.c_int]
+    lib.aqlm_ceiling_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
     return lib
+
+
+# aqlm_ceiling_lds modes: (name, bytes per lane access, what it stands for)
+LDS_MODES = (
+    ("read_b128_conflict_free", 16, "2x8 GEMV/GEMM A-operand reads from the bank-spread table"),
+    ("read_b128_four_addresses", 16, "2x8 GEMV activation fragments at one activation row"),
+    ("read_b64_random_128kib", 8, "codebook-sliced 1x16 GEMV lookups"),
+    ("read_b128_random_8kib", 16, "2x8 decode from an 8 KiB codebook copy (decoded-tile GEMM fill)"),
+    ("write_b128_conflict_free", 16, "tile and table writes"),
+)
+
+
+def lds_rates(torch, iters=1000):
+    """LDS access rates of the kernels' patterns (aqlm_ceiling_lds): clocks of
+    LDS time per wavefront access and bytes per clock per CU, with the shader
+    clock measured inside the kernel (core-clock cycles over the 100 MHz
+    real-time counter)."""
+    lib = _ceiling_lib()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {}
+    for mode, (name, width, what) in enumerate(LDS_MODES):
+        blocks = cus  # one workgroup of sixteen wavefronts per CU
+        sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+        clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):  # the first launch warms up; the second is reported
+            t0.record()
+            if lib.aqlm_ceiling_lds(mode, blocks, iters, sink.data_ptr(), clocks.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream) != 0:
+                raise RuntimeError("aqlm_ceiling_lds failed")
+            t1.record()
+            torch.cuda.synchronize()
+        wall_s = t0.elapsed_time(t1) * 1e-3
+        c = clocks.view(blocks, 2).cpu().double()
+        cyc = float(c[:, 0].median())
+        ghz = float((c[:, 0] / (c[:, 1] * 10.0)).median())
+        accesses = 16 * 16 * iters  # wavefront accesses per CU
+        clk = cyc / accesses
+        # the same from the launch's wall time (launch overhead included)
+        clk_wall = wall_s * ghz * 1e9 / accesses
+        out[name] = {"clk_per_wavefront_access": round(clk, 3),
+                     "bytes_per_clk_per_cu": round(64 * width / clk, 1),
+                     "lane_accesses_per_clk_per_cu": round(64 / clk, 2),
+                     "clk_per_wavefront_access_from_launch_time": round(clk_wall, 3),
+                     "wavefronts_per_cu": 16, "shader_clock_ghz": round(ghz, 3),
+                     "pattern_of": what}
+        del sink, clocks
+    return out
 
 
 def write_ceiling_us(torch, buf, nbytes, copies, reps):
@@ -602,6 +660,7 @@ def ceilings(torch, sizes):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     return {
         "read": out,
+        "lds": lds_rates(torch),
         "kernel": "aqlm_ceiling_read: 16-byte non-temporal loads, each byte once, a block of "
                   "256 threads per 4096 * loads_per_thread bytes",
         "gather_1mib": {"gathers_per_s": round(rate / 1e9, 2), "unit_rate": "G per s",
