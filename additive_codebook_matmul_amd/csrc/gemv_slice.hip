@@ -259,26 +259,30 @@ __global__ __launch_bounds__(T) void gemv_1x16_slice_kernel(SliceArgs A) {
 }
 
 // y[o] = fp16(scale[o] * (((p_0 + p_1) + p_2) + ... + p_7)) for every row of
-// every layer of the call (rows numbered across the layers in order).
+// every layer of the call. Each layer has blocks of its own (blocks
+// [blk_begin, blk_begin + ceil(out / 256)) of the launch), so the layer is a
+// function of the block index: its descriptor is read with scalar loads
+// rather than fetched per lane from memory before the partial sums.
 struct SliceReduceLayer {
   const float *part;
   const uint16_t *scales;
   uint16_t *y;
-  int out, row_begin;
+  int out, blk_begin;
 };
 struct SliceReduceArgs {
   SliceReduceLayer layer[kSlMaxGroup];
-  int n, rows;
+  int n;
 };
 
 __global__ __launch_bounds__(256) void gemv_1x16_slice_reduce(SliceReduceArgs A) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= A.rows) return;
+  const int blk = blockIdx.x;
   int li = 0;
+#pragma unroll 1
   for (int i = 1; i < A.n; ++i)
-    if (r >= A.layer[i].row_begin) li = i;
+    if (blk >= A.layer[i].blk_begin) li = i;
   const SliceReduceLayer &L = A.layer[li];
-  const int o = r - L.row_begin;
+  const int o = (blk - L.blk_begin) * 256 + (int)threadIdx.x;
+  if (o >= L.out) return;
   float v = L.part[o];
 #pragma unroll
   for (int m = 1; m < kSlMembers; ++m) v += L.part[(size_t)m * L.out + o];
@@ -385,14 +389,12 @@ hipError_t launch_gemv_slice(const LayerDesc *const *Ls, const uint16_t *const *
   }
   SliceReduceArgs R;
   R.n = n;
-  int rows = 0;
+  int blocks = 0;
   for (int i = 0; i < n; ++i) {
-    R.layer[i] = SliceReduceLayer{parts[i], Ls[i]->scales, ys[i], (int)Ls[i]->out, rows};
-    rows += (int)Ls[i]->out;
+    R.layer[i] = SliceReduceLayer{parts[i], Ls[i]->scales, ys[i], (int)Ls[i]->out, blocks};
+    blocks += (int)((Ls[i]->out + 255) / 256);
   }
-  R.rows = rows;
-  hipLaunchKernelGGL(gemv_1x16_slice_reduce, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                     stream, R);
+  hipLaunchKernelGGL(gemv_1x16_slice_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, R);
   return hipGetLastError();
 }
 
