@@ -109,9 +109,9 @@ __global__ __launch_bounds__(kThreads) void write_kernel(uint4 *__restrict__ buf
   }
 }
 
-// LDS patterns. Every lane keeps 16 byte offsets in registers (a random
-// sample of its pattern, drawn by an LCG at the start) and cycles through
-// them; an empty asm statement marks each offset as changed before its use,
+// LDS patterns. Every lane keeps 16 offsets into the table in registers (a
+// sample of its pattern; the random patterns draw theirs with an LCG at the
+// start) and cycles through them; an empty asm statement marks each offset as changed before its use,
 // so the accesses stay in the loop, and a read feeds one three-operand add
 // per 8 bytes into the lane's fold (every byte of the read is used, so its
 // width is kept).
@@ -264,9 +264,10 @@ CEIL_API int aqlm_ceiling_lds_bytes(int mode) {
 
 // LDS access rate of `mode` (see lds_kernel): `blocks` workgroups of 1024
 // threads (sixteen wavefronts; one per CU when `blocks` is the CU count),
-// each lane issuing 16 * iters accesses. clocks receives, per block, the core-clock cycles and
-// the 100 MHz real-time ticks between the block's first and last access
-// (2 * blocks words); sink must hold `blocks` words. 0 on success.
+// each lane issuing 16 * iters accesses. clocks receives, per block, the
+// core-clock cycles and the 100 MHz real-time ticks from just before the
+// access loop to the barrier after it (2 * blocks words); sink must hold
+// `blocks` words. 0 on success.
 CEIL_API int aqlm_ceiling_lds(int mode, int blocks, int iters, uint32_t *sink,
                               unsigned long long *clocks, void *stream) {
   const int bytes = aqlm_ceiling_lds_bytes(mode);
