@@ -401,11 +401,254 @@ int device_cus() {
   return cus;
 }
 
+
+// ---------------------------------------------------------------------------
+// One activation row, rows of at most 512 groups: one output row per
+// wavefront at a time.
+//
+// The matrix core's 16 A rows are 16 segments of ONE output row. In step t
+// (t = 0..7) lane L = 16 q + r feeds group g(L, t) = 8 r + 128 q + t of the
+// row: the fp16 sum of the group's two codewords as its A operand and the
+// group's 8 activations as its B operand (row r of A, column r of B). The
+// result's diagonal element D[r][r] then collects the products of exactly
+// the groups of segment r, and the row's total is the sum of the diagonal;
+// over the 8 steps and 64 lanes every group of the row is taken once
+// (8 r + t runs over 0..127, 128 q over the four quarters). Against the tile
+// form above:
+//   * a lane's codes for the whole row are one 16-byte load (groups 8 r +
+//     128 q .. + 7, at byte 16 r + 256 q), so the wavefront's 64 loads are
+//     the row's 1 KiB in order, whole cache lines (the tile form reads 64
+//     bytes of each of 16 rows per load instruction, which costs the
+//     texture-address unit about three times as long per instruction, and
+//     every wavefront of a CU issues its code loads at once at the start);
+//   * a lane's activation fragments do not depend on the row: its 8
+//     fragments (32 registers) are read from LDS once and serve every row,
+//     so a row costs two 16-byte LDS reads per step instead of three;
+//   * a row needs no other wavefront: no partial sums in LDS and no barrier
+//     after the prologue. The diagonal is gathered by quad broadcasts (the
+//     four diagonal elements of a quad sit in its four lanes) and the four
+//     diagonal quads are added in a fixed order, so a row's result does not
+//     depend on which wavefront or workgroup computes it.
+// The staged activations keep 16 bytes of padding after every 8 groups, so
+// the 16 lanes of a 16-byte LDS pass (consecutive r) hit distinct banks.
+constexpr int kRThreads = 1024;
+constexpr int kRWaves = kRThreads / 64;
+constexpr int kRGroups = 512;                   // groups per row the form serves
+constexpr int kRXBytes = kRGroups / 8 * 144;    // staged activations with padding
+
+__device__ __forceinline__ uint32_t rows_x_off(uint32_t g) { return g * 16u + (g >> 3) * 16u; }
+
+struct RowsLayer {
+  const uint8_t *codes;
+  const uint16_t *books;
+  const uint16_t *scales;
+  const uint16_t *x;
+  uint16_t *y;
+  int out, groups;
+  int blk_begin, blk_count;  // blocks [blk_begin, blk_begin + blk_count) serve this layer
+};
+
+struct RowsGroup {
+  RowsLayer layer[kMaxMfmaGroup];
+  int n;
+};
+
+// RD: rows of codes in flight per wavefront.
+template <int RD>
+__global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
+  __shared__ __attribute__((aligned(16))) uint8_t table[kMTable];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t *xs = lds;
+  uint32_t *big_flags = reinterpret_cast<uint32_t *>(lds + kRXBytes);
+
+  int l = 0;
+#pragma unroll 1
+  for (int i = 1; i < G.n; ++i)
+    if ((int)blockIdx.x >= G.layer[i].blk_begin) l = i;
+  const RowsLayer &L = G.layer[l];
+  const int blk = (int)blockIdx.x - L.blk_begin;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const uint32_t row_bytes = (uint32_t)L.groups * 2u;
+  // this workgroup's rows [r0, r1); wavefront w takes r0 + w, r0 + w + 16, ...
+  const int r0 = (int)((int64_t)L.out * blk / L.blk_count);
+  const int r1 = (int)((int64_t)L.out * (blk + 1) / L.blk_count);
+  const int nrows = r1 > r0 + wave ? (r1 - r0 - wave + kRWaves - 1) / kRWaves : 0;
+
+  // Prologue, in issue order: the codebook entry of threads 0..511 and the
+  // activation vector of threads 0..511 (L2), then the codes and row scales
+  // of the first RD rows (HBM); the LDS writes below wait for L2 only.
+  const int tt = tid & 511;
+  const int tm = (tt >> 3) & 1;                  // table entry: codebook tm,
+  const int tc = (tt & 7) | ((tt >> 4) << 3);    // code value tc
+  const Rsrc rx = make_rsrc(L.x, (uint32_t)L.groups * 16u);
+  uint4 book_v = make_uint4(0u, 0u, 0u, 0u), xv = make_uint4(0u, 0u, 0u, 0u);
+  if (kRThreads <= 512 || tid < 512) {  // wavefronts past the first eight load neither
+    book_v = reinterpret_cast<const uint4 *>(L.books)[tm * 256 + tc];
+    xv = buf_load16(rx, (uint32_t)tt * 16u);  // zero past the row's groups
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const Rsrc rc = make_rsrc(L.codes, (uint32_t)L.out * row_bytes);
+  const Rsrc rs = make_rsrc(L.scales, (uint32_t)L.out * 2u);
+  const uint32_t lane_g = (uint32_t)(8 * r + 128 * q);  // the first of the lane's 8 groups
+  const bool lane_ok = lane_g < (uint32_t)L.groups;     // groups is a multiple of 8
+  uint4 cw[RD];
+  uint32_t sv[RD];
+  auto load_row = [&](int k, uint4 &c, uint32_t &sc) {
+    const bool ok = k < nrows;
+    const uint32_t row = (uint32_t)(r0 + wave + k * kRWaves);
+    c = buf_load16_nt(rc, (ok && lane_ok) ? row * row_bytes + lane_g * 2u : kMOOB);
+    sc = buf_load_u16(rs, ok ? row * 2u : kMOOB);
+  };
+#pragma unroll
+  for (int u = 0; u < RD; ++u) load_row(u, cw[u], sv[u]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the bank-spread table (the tile form's layout), the activations (zero
+  // past the row's groups), the overflow-guard flags
+  if (tid < 512) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + ((j + tid) & 7) * 16) = book_v;
+  }
+  if (tid < kRGroups) *reinterpret_cast<uint4 *>(xs + rows_x_off((uint32_t)tid)) = xv;
+  publish_flag(big_flags, tid < 512 && has_large_half(book_v));
+  __syncthreads();
+  const bool halved = read_flag(big_flags, kRWaves);
+  if (halved) {
+    const uint4 hv = hhalf8(book_v);
+    if (tid < 512) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + ((j + tid) & 7) * 16) = hv;
+    }
+    __syncthreads();
+  }
+  const float total_mul = halved ? 2.0f : 1.0f;
+
+  // this lane's activation fragments, the same for every row
+  uint4 b[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) b[t] = *reinterpret_cast<const uint4 *>(xs + rows_x_off(lane_g + t));
+
+  const uint32_t baseA = (uint32_t)r * 16u, baseB = (uint32_t)(r ^ 8) * 16u;
+  const uint32_t mA = (uint32_t)(r >> 3), mB = mA ^ 1u;
+  const uint32_t selA[2] = {0x0C0C0000u | ((4u + mA) << 8), 0x0C0C0000u | ((6u + mA) << 8)};
+  const uint32_t selB[2] = {0x0C0C0000u | ((4u + mB) << 8), 0x0C0C0000u | ((6u + mB) << 8)};
+  const bool diag_quad = ((lane >> 2) >> 2) == ((lane >> 2) & 3);
+
+  // The row's total (in lane 63): 8 steps, two accumulators so that
+  // consecutive MFMAs are independent, then the diagonal.
+  auto row_total = [&](const uint4 &c) {
+    float4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int h = 0; h < 8; h += 4) {
+      uint4 a0[4], a1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = h + u;
+        const uint32_t addrA = __builtin_amdgcn_perm(w[s >> 1], baseA, selA[s & 1]);
+        const uint32_t addrB = __builtin_amdgcn_perm(w[s >> 1], baseB, selB[s & 1]);
+        a0[u] = *reinterpret_cast<const uint4 *>(table + addrA);
+        a1[u] = *reinterpret_cast<const uint4 *>(table + addrB);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const half8_t wv = __builtin_bit_cast(half8_t, hadd8(a0[u], a1[u]));
+        if (u & 1)
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(half8_t, b[h + u]),
+                                                        acc1, 0, 0, 0);
+        else
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(half8_t, b[h + u]),
+                                                        acc0, 0, 0, 0);
+      }
+    }
+    const float4_t acc = acc0 + acc1;
+    // lane 4 j + e of a diagonal quad j holds D[4 k + e][4 k + e] (k = j / 5)
+    // in element e
+    float v = dpp<kDppQuadBcast0>(acc[0]) + dpp<kDppQuadBcast1>(acc[1]);
+    v += dpp<kDppQuadBcast2>(acc[2]);
+    v += dpp<kDppQuadBcast3>(acc[3]);
+    return quads_sum_to_lane63(diag_quad ? v : 0.0f);
+  };
+
+  // rows k, k + 1, ...: row k's codes are in ring slot k % RD, refilled with
+  // row k + RD once its total is taken
+  for (int k0 = 0; k0 < nrows; k0 += RD) {
+#pragma unroll
+    for (int u = 0; u < RD; ++u) {
+      if (k0 + u < nrows) {
+        const float v = row_total(cw[u]);
+        const uint32_t sc = sv[u];
+        load_row(k0 + u + RD, cw[u], sv[u]);
+        if (lane == 63)
+          L.y[r0 + wave + (k0 + u) * kRWaves] = (uint16_t)f2h((v * total_mul) * h2f(sc));
+      }
+    }
+  }
+}
+
+template <int RD>
+hipError_t launch_rows(const RowsGroup &G, int blocks, hipStream_t stream) {
+  static std::atomic<uint64_t> done{0};
+  auto k = gemv_2x8_rows_kernel<RD>;
+  constexpr size_t dyn = kRXBytes + kRWaves * 4;
+  hipError_t e = allow_lds(k, kMaxLds - kMTable, done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3(blocks), dim3(kRThreads), dyn, stream, G);
+  return hipGetLastError();
+}
+
+// The layers (all accepted by gemv_2x8_rows_fits), one launch: workgroups
+// split over the layers in proportion to their rows, one workgroup per CU
+// in all, at most one per 16 rows.
+hipError_t launch_rows_group(const LayerDesc *const *Ls, const uint16_t *const *xs,
+                             uint16_t *const *ys, int n, hipStream_t stream) {
+  RowsGroup G;
+  G.n = n;
+  const int cus = device_cus();
+  double total = 0;
+  for (int i = 0; i < n; ++i) total += (double)Ls[i]->out;
+  int begin = 0, max_rpw = 1;
+  for (int i = 0; i < n; ++i) {
+    const LayerDesc &L = *Ls[i];
+    const int most = (int)((L.out + kRWaves - 1) / kRWaves);
+    int blocks = (int)((double)cus * (double)L.out / total + 0.5);
+    if (blocks > most) blocks = most;
+    if (blocks < 1) blocks = 1;
+    // rows per wavefront: the longest share of any workgroup of this layer
+    const int rows_per_block = (int)((L.out + blocks - 1) / blocks);
+    const int rpw = (rows_per_block + kRWaves - 1) / kRWaves;
+    if (rpw > max_rpw) max_rpw = rpw;
+    G.layer[i] = RowsLayer{static_cast<const uint8_t *>(L.codes), L.books, L.scales, xs[i], ys[i],
+                           (int)L.out, (int)L.groups, begin, blocks};
+    begin += blocks;
+  }
+  if (max_rpw <= 1) return launch_rows<1>(G, begin, stream);
+  if (max_rpw <= 2) return launch_rows<2>(G, begin, stream);
+  if (max_rpw <= 3) return launch_rows<3>(G, begin, stream);
+  return launch_rows<4>(G, begin, stream);
+}
+
 }  // namespace
+
+// True when the one-row-per-wavefront form serves this layer: one
+// activation row, rows of at most 512 groups in whole 8-group lane pieces,
+// 32-bit byte offsets.
+bool gemv_2x8_rows_fits(const LayerDesc &L, int batch) {
+  if (L.scheme != Scheme::k2x8 || batch != 1) return false;
+  if (L.groups % 8 != 0 || L.groups > kRGroups) return false;
+  return (L.out + 1) * L.groups * 2 < ((int64_t)1 << 31);
+}
 
 // True when the matrix-core GEMV serves this layer and batch.
 bool gemv_2x8_mfma_fits(const LayerDesc &L, int batch) {
   if (L.scheme != Scheme::k2x8 || batch < 1 || batch > 8) return false;
+  if (gemv_2x8_rows_fits(L, batch)) return true;
   if (L.groups % 32 != 0 || mfma_class(L.groups / 32) < 0) return false;
   const int rows = batch <= 1 ? 1 : (batch <= 2 ? 2 : (batch <= 4 ? 4 : 8));
   if (mfma_lds_bytes(rows, (int)L.in) > kMaxLds) return false;
@@ -494,6 +737,28 @@ hipError_t mfma_group_batch(const LayerDesc *const *Ls, const uint16_t *const *x
 hipError_t launch_gemv_2x8_mfma_batched(const LayerDesc *Ls, const uint16_t *const *xs,
                                         uint16_t *const *ys, int n, int batch, bool *done,
                                         hipStream_t stream) {
+  {
+    // one activation row, rows of at most 512 groups: one-row-per-wavefront form
+    const LayerDesc *sel[kMaxMfmaGroup];
+    const uint16_t *sx[kMaxMfmaGroup];
+    uint16_t *sy[kMaxMfmaGroup];
+    int m = 0;
+    for (int i = 0; i <= n; ++i) {
+      const bool take = i < n && !done[i] && gemv_2x8_rows_fits(Ls[i], batch);
+      if (take) {
+        sel[m] = &Ls[i];
+        sx[m] = xs[i];
+        sy[m] = ys[i];
+        ++m;
+        done[i] = true;
+      }
+      if (m == kMaxMfmaGroup || (i == n && m > 0)) {
+        const hipError_t e = launch_rows_group(sel, sx, sy, m, stream);
+        if (e != hipSuccess) return e;
+        m = 0;
+      }
+    }
+  }
   for (int cls = 0; cls < 4; ++cls) {
     const LayerDesc *sel[kMaxMfmaGroup];
     const uint16_t *sx[kMaxMfmaGroup];
@@ -524,6 +789,12 @@ hipError_t launch_gemv_2x8_mfma_batched(const LayerDesc *Ls, const uint16_t *con
 
 hipError_t launch_gemv_2x8_mfma(const LayerDesc &L, const uint16_t *x, int batch, uint16_t *y,
                                 hipStream_t stream) {
+  if (gemv_2x8_rows_fits(L, batch)) {
+    const LayerDesc *ls[1] = {&L};
+    const uint16_t *xs[1] = {x};
+    uint16_t *ys[1] = {y};
+    return launch_rows_group(ls, xs, ys, 1, stream);
+  }
   if (batch <= 1) return launch_mfma_batch<1>(L, x, batch, y, stream);
   if (batch <= 2) return launch_mfma_batch<2>(L, x, batch, y, stream);
   if (batch <= 4) return launch_mfma_batch<4>(L, x, batch, y, stream);

@@ -59,7 +59,8 @@ SCHEME_SPECS = {
     "2x8": {
         "workload": "llama2_7b_2x8",
         "scheme": "2x8 (M=2, B=8, g=8)",
-        "kernel": "gemv_2x8_mfma_group_kernel (grouped 2x8 GEMV on the matrix cores, batch 1)",
+        "kernel": "gemv_2x8_rows_kernel (2x8 GEMV on the matrix cores, one output row per "
+                  "wavefront, batch 1; the grouped q,k,v and gate,up calls)",
         "dominant": (("q", "k", "v"), ("gate", "up")),
         "source": "gemv_mfma.hip",
         "traffic": os.path.join(ROOT, "profiles", "gemv_2x8_llama2_7b_b1_traffic.json"),
