@@ -403,8 +403,8 @@ int device_cus() {
 
 
 // ---------------------------------------------------------------------------
-// One activation row, rows of at most 512 groups: one output row per
-// wavefront at a time.
+// One activation row, rows of at most 2048 groups (in <= 16384): one output
+// row per wavefront at a time.
 //
 // The matrix core's 16 A rows are 16 segments of ONE output row. In step t
 // (t = 0..7) lane L = 16 q + r feeds group g(L, t) = 8 r + 128 q + t of the
@@ -433,8 +433,9 @@ int device_cus() {
 // the 16 lanes of a 16-byte LDS pass (consecutive r) hit distinct banks.
 constexpr int kRThreads = 1024;
 constexpr int kRWaves = kRThreads / 64;
-constexpr int kRGroups = 512;                   // groups per row the form serves
-constexpr int kRXBytes = kRGroups / 8 * 144;    // staged activations with padding
+constexpr int kRGroups = 512;                   // groups of one pass over a row
+constexpr int kRMaxPasses = 4;                  // rows of up to 2048 groups (in <= 16384)
+constexpr int kRXBytes = kRGroups / 8 * 144;    // staged activations of one pass, with padding
 
 __device__ __forceinline__ uint32_t rows_x_off(uint32_t g) { return g * 16u + (g >> 3) * 16u; }
 
@@ -453,13 +454,16 @@ struct RowsGroup {
   int n;
 };
 
-// RD: rows of codes in flight per wavefront.
-template <int RD>
+// RD: rows of codes in flight per wavefront; NP: passes of 512 groups per
+// row (a row of more than 512 groups is taken pass by pass, each pass as
+// above; the activation fragments of a lane are then read from LDS in every
+// step rather than kept, since NP x 32 registers would not fit).
+template <int RD, int NP>
 __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   __shared__ __attribute__((aligned(16))) uint8_t table[kMTable];
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *xs = lds;
-  uint32_t *big_flags = reinterpret_cast<uint32_t *>(lds + kRXBytes);
+  uint32_t *big_flags = reinterpret_cast<uint32_t *>(lds + NP * kRXBytes);
 
   int l = 0;
 #pragma unroll 1
@@ -484,23 +488,37 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   const int tm = (tt >> 3) & 1;                  // table entry: codebook tm,
   const int tc = (tt & 7) | ((tt >> 4) << 3);    // code value tc
   const Rsrc rx = make_rsrc(L.x, (uint32_t)L.groups * 16u);
-  uint4 book_v = make_uint4(0u, 0u, 0u, 0u), xv = make_uint4(0u, 0u, 0u, 0u);
-  if (kRThreads <= 512 || tid < 512) {  // wavefronts past the first eight load neither
+  // activation vectors (one group's 8 values each) staged per thread: group
+  // tid + 1024 i; one-pass rows need only the first eight wavefronts
+  constexpr int NXV = (NP * kRGroups + kRThreads - 1) / kRThreads;
+  uint4 book_v = make_uint4(0u, 0u, 0u, 0u), xv[NXV];
+#pragma unroll
+  for (int i = 0; i < NXV; ++i) xv[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (kRThreads <= 512 || tid < 512)  // wavefronts past the first eight build no table
     book_v = reinterpret_cast<const uint4 *>(L.books)[tm * 256 + tc];
-    xv = buf_load16(rx, (uint32_t)tt * 16u);  // zero past the row's groups
+  if (NP > 1 || tid < kRGroups) {
+#pragma unroll
+    for (int i = 0; i < NXV; ++i) {  // zero past the row's groups
+      const uint32_t g = (uint32_t)(tid + i * kRThreads);
+      xv[i] = buf_load16(rx, g < (uint32_t)(NP * kRGroups) ? g * 16u : kMOOB);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
   const Rsrc rc = make_rsrc(L.codes, (uint32_t)L.out * row_bytes);
   const Rsrc rs = make_rsrc(L.scales, (uint32_t)L.out * 2u);
-  const uint32_t lane_g = (uint32_t)(8 * r + 128 * q);  // the first of the lane's 8 groups
-  const bool lane_ok = lane_g < (uint32_t)L.groups;     // groups is a multiple of 8
-  uint4 cw[RD];
+  const uint32_t lane_g = (uint32_t)(8 * r + 128 * q);  // the first of the lane's 8 groups in a pass
+  uint4 cw[RD][NP];
   uint32_t sv[RD];
-  auto load_row = [&](int k, uint4 &c, uint32_t &sc) {
+  auto load_row = [&](int k, uint4 (&c)[NP], uint32_t &sc) {
     const bool ok = k < nrows;
     const uint32_t row = (uint32_t)(r0 + wave + k * kRWaves);
-    c = buf_load16_nt(rc, (ok && lane_ok) ? row * row_bytes + lane_g * 2u : kMOOB);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t g = lane_g + (uint32_t)(p * kRGroups);
+      // groups is a multiple of 8: a lane's 8 groups are all in the row or all past it
+      c[p] = buf_load16_nt(rc, (ok && g < (uint32_t)L.groups) ? row * row_bytes + g * 2u : kMOOB);
+    }
     sc = buf_load_u16(rs, ok ? row * 2u : kMOOB);
   };
 #pragma unroll
@@ -514,7 +532,11 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + ((j + tid) & 7) * 16) = book_v;
   }
-  if (tid < kRGroups) *reinterpret_cast<uint4 *>(xs + rows_x_off((uint32_t)tid)) = xv;
+#pragma unroll
+  for (int i = 0; i < NXV; ++i) {
+    const uint32_t g = (uint32_t)(tid + i * kRThreads);
+    if (g < (uint32_t)(NP * kRGroups)) *reinterpret_cast<uint4 *>(xs + rows_x_off(g)) = xv[i];
+  }
   publish_flag(big_flags, tid < 512 && has_large_half(book_v));
   __syncthreads();
   const bool halved = read_flag(big_flags, kRWaves);
@@ -529,10 +551,13 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   }
   const float total_mul = halved ? 2.0f : 1.0f;
 
-  // this lane's activation fragments, the same for every row
-  uint4 b[8];
+  // this lane's activation fragments, the same for every row (kept in
+  // registers for one-pass rows)
+  uint4 b[NP == 1 ? 8 : 1];
+  if constexpr (NP == 1) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) b[t] = *reinterpret_cast<const uint4 *>(xs + rows_x_off(lane_g + t));
+    for (int t = 0; t < 8; ++t) b[t] = *reinterpret_cast<const uint4 *>(xs + rows_x_off(lane_g + t));
+  }
 
   const uint32_t baseA = (uint32_t)r * 16u, baseB = (uint32_t)(r ^ 8) * 16u;
   const uint32_t mA = (uint32_t)(r >> 3), mB = mA ^ 1u;
@@ -542,29 +567,40 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
 
   // The row's total (in lane 63): 8 steps, two accumulators so that
   // consecutive MFMAs are independent, then the diagonal.
-  auto row_total = [&](const uint4 &c) {
+  auto row_total = [&](const uint4 (&c)[NP]) {
     float4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-    for (int h = 0; h < 8; h += 4) {
-      uint4 a0[4], a1[4];
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t w[4] = {c[p].x, c[p].y, c[p].z, c[p].w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = h + u;
-        const uint32_t addrA = __builtin_amdgcn_perm(w[s >> 1], baseA, selA[s & 1]);
-        const uint32_t addrB = __builtin_amdgcn_perm(w[s >> 1], baseB, selB[s & 1]);
-        a0[u] = *reinterpret_cast<const uint4 *>(table + addrA);
-        a1[u] = *reinterpret_cast<const uint4 *>(table + addrB);
-      }
+      for (int h = 0; h < 8; h += 4) {
+        uint4 a0[4], a1[4], bb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const half8_t wv = __builtin_bit_cast(half8_t, hadd8(a0[u], a1[u]));
-        if (u & 1)
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(half8_t, b[h + u]),
-                                                        acc1, 0, 0, 0);
-        else
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(half8_t, b[h + u]),
-                                                        acc0, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+          const int s = h + u;
+          const uint32_t addrA = __builtin_amdgcn_perm(w[s >> 1], baseA, selA[s & 1]);
+          const uint32_t addrB = __builtin_amdgcn_perm(w[s >> 1], baseB, selB[s & 1]);
+          a0[u] = *reinterpret_cast<const uint4 *>(table + addrA);
+          a1[u] = *reinterpret_cast<const uint4 *>(table + addrB);
+          if constexpr (NP == 1)
+            bb[u] = b[s];
+          else
+            bb[u] = *reinterpret_cast<const uint4 *>(
+                xs + rows_x_off(lane_g + (uint32_t)(p * kRGroups + s)));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const half8_t wv = __builtin_bit_cast(half8_t, hadd8(a0[u], a1[u]));
+          if (u & 1)
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(half8_t, bb[u]),
+                                                          acc1, 0, 0, 0);
+          else
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, __builtin_bit_cast(half8_t, bb[u]),
+                                                          acc0, 0, 0, 0);
+        }
+        // keep each half-pass's LDS reads next to its MFMAs (hoisting the
+        // reads of later passes costs registers and spills)
+        if constexpr (NP > 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
     const float4_t acc = acc0 + acc1;
@@ -592,18 +628,19 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   }
 }
 
-template <int RD>
+template <int RD, int NP>
 hipError_t launch_rows(const RowsGroup &G, int blocks, hipStream_t stream) {
   static std::atomic<uint64_t> done{0};
-  auto k = gemv_2x8_rows_kernel<RD>;
-  constexpr size_t dyn = kRXBytes + kRWaves * 4;
+  auto k = gemv_2x8_rows_kernel<RD, NP>;
+  constexpr size_t dyn = NP * kRXBytes + kRWaves * 4;
   hipError_t e = allow_lds(k, kMaxLds - kMTable, done);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(blocks), dim3(kRThreads), dyn, stream, G);
   return hipGetLastError();
 }
 
-// The layers (all accepted by gemv_2x8_rows_fits), one launch: workgroups
+// The layers (all accepted by gemv_2x8_rows_fits, all with the same number of
+// 512-group passes), one launch: workgroups
 // split over the layers in proportion to their rows, one workgroup per CU
 // in all, at most one per 16 rows.
 hipError_t launch_rows_group(const LayerDesc *const *Ls, const uint16_t *const *xs,
@@ -628,20 +665,28 @@ hipError_t launch_rows_group(const LayerDesc *const *Ls, const uint16_t *const *
                            (int)L.out, (int)L.groups, begin, blocks};
     begin += blocks;
   }
-  if (max_rpw <= 1) return launch_rows<1>(G, begin, stream);
-  if (max_rpw <= 2) return launch_rows<2>(G, begin, stream);
-  if (max_rpw <= 3) return launch_rows<3>(G, begin, stream);
-  return launch_rows<4>(G, begin, stream);
+  // every layer of the launch has the same pass count
+  switch ((int)((Ls[0]->groups + kRGroups - 1) / kRGroups)) {
+    case 1:
+      if (max_rpw <= 1) return launch_rows<1, 1>(G, begin, stream);
+      if (max_rpw <= 2) return launch_rows<2, 1>(G, begin, stream);
+      if (max_rpw <= 3) return launch_rows<3, 1>(G, begin, stream);
+      return launch_rows<4, 1>(G, begin, stream);
+    case 2: return launch_rows<1, 2>(G, begin, stream);
+    case 3: return launch_rows<1, 3>(G, begin, stream);
+    case 4: return launch_rows<1, 4>(G, begin, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 // True when the one-row-per-wavefront form serves this layer: one
-// activation row, rows of at most 512 groups in whole 8-group lane pieces,
+// activation row, rows of at most 2048 groups in whole 8-group lane pieces,
 // 32-bit byte offsets.
 bool gemv_2x8_rows_fits(const LayerDesc &L, int batch) {
   if (L.scheme != Scheme::k2x8 || batch != 1) return false;
-  if (L.groups % 8 != 0 || L.groups > kRGroups) return false;
+  if (L.groups % 8 != 0 || L.groups > kRMaxPasses * kRGroups) return false;
   return (L.out + 1) * L.groups * 2 < ((int64_t)1 << 31);
 }
 
@@ -738,13 +783,16 @@ hipError_t launch_gemv_2x8_mfma_batched(const LayerDesc *Ls, const uint16_t *con
                                         uint16_t *const *ys, int n, int batch, bool *done,
                                         hipStream_t stream) {
   {
-    // one activation row, rows of at most 512 groups: one-row-per-wavefront form
+    // one activation row, rows of at most 2048 groups: the one-row-per-wavefront
+    // form, one launch per pass count
     const LayerDesc *sel[kMaxMfmaGroup];
     const uint16_t *sx[kMaxMfmaGroup];
     uint16_t *sy[kMaxMfmaGroup];
     int m = 0;
+    for (int np = 1; np <= kRMaxPasses; ++np)
     for (int i = 0; i <= n; ++i) {
-      const bool take = i < n && !done[i] && gemv_2x8_rows_fits(Ls[i], batch);
+      const bool take = i < n && !done[i] && gemv_2x8_rows_fits(Ls[i], batch) &&
+                        (Ls[i].groups + kRGroups - 1) / kRGroups == np;
       if (take) {
         sel[m] = &Ls[i];
         sx[m] = xs[i];
