@@ -671,6 +671,11 @@ hipError_t launch_rows_group(const LayerDesc *const *Ls, const uint16_t *const *
       if (max_rpw <= 1) return launch_rows<1, 1>(G, begin, stream);
       if (max_rpw <= 2) return launch_rows<2, 1>(G, begin, stream);
       if (max_rpw <= 3) return launch_rows<3, 1>(G, begin, stream);
+      // five or six rows per wavefront: all of them in flight (gate,up call
+      // 10.65-11.10 -> 10.46-10.57 us against four); more rows stream
+      // through a ring of four (eight in flight made the ten-row
+      // whole-block call slower, 23.7-24.2 -> 25.2-25.8 us)
+      if (max_rpw == 5 || max_rpw == 6) return launch_rows<6, 1>(G, begin, stream);
       return launch_rows<4, 1>(G, begin, stream);
     case 2: return launch_rows<1, 2>(G, begin, stream);
     case 3: return launch_rows<1, 3>(G, begin, stream);
