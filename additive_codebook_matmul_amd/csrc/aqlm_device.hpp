@@ -35,6 +35,10 @@ __device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t num_bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes,
                                            0x00020000);
 }
+// a 2-byte store; dropped by the hardware where off is out of range
+__device__ __forceinline__ void buf_store_u16(Rsrc r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
 __device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);

@@ -439,6 +439,24 @@ constexpr int kRXBytes = kRGroups / 8 * 144;    // staged activations of one pas
 
 __device__ __forceinline__ uint32_t rows_x_off(uint32_t g) { return g * 16u + (g >> 3) * 16u; }
 
+// An LDS word read as one value for the whole wavefront.
+__device__ __forceinline__ uint32_t lds_read_word(uint32_t *w) {
+  return __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+// Waits until an LDS counter of the workgroup reaches n. The wait is bounded
+// (about 0.1 s) so that a kernel always ends; the counters it serves reach n
+// within microseconds, because every wavefront adds its count unconditionally.
+// LDS operations that follow in program order are issued after it returns.
+__device__ __forceinline__ void lds_wait_count(uint32_t *w, uint32_t n) {
+#pragma unroll 1
+  for (int i = 0; i < (1 << 22); ++i) {
+    if (lds_read_word(w) >= n) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
 struct RowsLayer {
   const uint8_t *codes;
   const uint16_t *books;
@@ -463,7 +481,14 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   __shared__ __attribute__((aligned(16))) uint8_t table[kMTable];
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *xs = lds;
-  uint32_t *big_flags = reinterpret_cast<uint32_t *>(lds + NP * kRXBytes);
+  // hand-over words: [0] the overflow guard (set if any codebook entry has a
+  // large half), [1] table-building wavefronts that have published their
+  // part of it, [2] wavefronts whose LDS writes are done
+  uint32_t *sy = reinterpret_cast<uint32_t *>(lds + NP * kRXBytes);
+  if (threadIdx.x < 3) sy[threadIdx.x] = 0u;
+  // the wavefronts of a workgroup start together: this barrier is short, and
+  // it is the only one
+  __syncthreads();
 
   int l = 0;
 #pragma unroll 1
@@ -481,33 +506,50 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   const int r1 = (int)((int64_t)L.out * (blk + 1) / L.blk_count);
   const int nrows = r1 > r0 + wave ? (r1 - r0 - wave + kRWaves - 1) / kRWaves : 0;
 
-  // Prologue, in issue order: the codebook entry of threads 0..511 and the
-  // activation vector of threads 0..511 (L2), then the codes and row scales
-  // of the first RD rows (HBM); the LDS writes below wait for L2 only.
-  const int tt = tid & 511;
-  const int tm = (tt >> 3) & 1;                  // table entry: codebook tm,
-  const int tc = (tt & 7) | ((tt >> 4) << 3);    // code value tc
-  const Rsrc rx = make_rsrc(L.x, (uint32_t)L.groups * 16u);
-  // activation vectors (one group's 8 values each) staged per thread: group
-  // tid + 1024 i; one-pass rows need only the first eight wavefronts
-  constexpr int NXV = (NP * kRGroups + kRThreads - 1) / kRThreads;
-  uint4 book_v = make_uint4(0u, 0u, 0u, 0u), xv[NXV];
-#pragma unroll
-  for (int i = 0; i < NXV; ++i) xv[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (kRThreads <= 512 || tid < 512)  // wavefronts past the first eight build no table
-    book_v = reinterpret_cast<const uint4 *>(L.books)[tm * 256 + tc];
-  if (NP > 1 || tid < kRGroups) {
-#pragma unroll
-    for (int i = 0; i < NXV; ++i) {  // zero past the row's groups
-      const uint32_t g = (uint32_t)(tid + i * kRThreads);
-      xv[i] = buf_load16(rx, g < (uint32_t)(NP * kRGroups) ? g * 16u : kMOOB);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
+  // Prologue. Wavefronts 0..7 build the codebook table and stage the
+  // activations; 8..15 write nothing to LDS. A wavefront stalls at a vector
+  // load until the texture-address unit accepts it, and a CU's code loads
+  // keep that unit busy for a microsecond or more, so the builders queue
+  // their codes only after their LDS writes, while the others queue theirs at
+  // once. There is no barrier: each wavefront counts itself done in LDS (after
+  // its LDS writes, if any) and waits for all sixteen counts before its first
+  // table read.
+  const bool builder = wave < 8;
+  const int tm = (tid >> 3) & 1;                  // table entry: codebook tm,
+  const int tc = (tid & 7) | ((tid >> 4) << 3);   // code value tc (builders)
   const Rsrc rc = make_rsrc(L.codes, (uint32_t)L.out * row_bytes);
   const Rsrc rs = make_rsrc(L.scales, (uint32_t)L.out * 2u);
   const uint32_t lane_g = (uint32_t)(8 * r + 128 * q);  // the first of the lane's 8 groups in a pass
+  if (builder) {
+    // activation vectors (one group's 8 values each): groups tid + 512 i,
+    // zero past the row's groups
+    const Rsrc rx = make_rsrc(L.x, (uint32_t)L.groups * 16u);
+    const uint4 book_v = reinterpret_cast<const uint4 *>(L.books)[tm * 256 + tc];
+    uint4 xv[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) xv[i] = buf_load16(rx, (uint32_t)(tid + i * 512) * 16u);
+    // the overflow guard is known once all eight builders have published
+    const bool big = __ballot(has_large_half(book_v)) != 0;
+    if (lane == 0) {
+      if (big) __hip_atomic_fetch_or(&sy[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      asm volatile("" ::: "memory");
+      __hip_atomic_fetch_add(&sy[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    lds_wait_count(&sy[1], 8u);
+    // codebooks large enough for the fp16 codeword sum to overflow: a halved
+    // table, doubled row totals (overflow guard, aqlm_device.hpp)
+    const uint4 tv = lds_read_word(&sy[0]) != 0u ? hhalf8(book_v) : book_v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + ((j + tid) & 7) * 16) = tv;
+#pragma unroll
+    for (int i = 0; i < NP; ++i)
+      *reinterpret_cast<uint4 *>(xs + rows_x_off((uint32_t)(tid + i * 512))) = xv[i];
+  }
+  // LDS operations of a wavefront complete in order: the count follows its writes
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) __hip_atomic_fetch_add(&sy[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+
   uint4 cw[RD][NP];
   uint32_t sv[RD];
   auto load_row = [&](int k, uint4 (&c)[NP], uint32_t &sc) {
@@ -523,32 +565,8 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   };
 #pragma unroll
   for (int u = 0; u < RD; ++u) load_row(u, cw[u], sv[u]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // the bank-spread table (the tile form's layout), the activations (zero
-  // past the row's groups), the overflow-guard flags
-  if (tid < 512) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + ((j + tid) & 7) * 16) = book_v;
-  }
-#pragma unroll
-  for (int i = 0; i < NXV; ++i) {
-    const uint32_t g = (uint32_t)(tid + i * kRThreads);
-    if (g < (uint32_t)(NP * kRGroups)) *reinterpret_cast<uint4 *>(xs + rows_x_off(g)) = xv[i];
-  }
-  publish_flag(big_flags, tid < 512 && has_large_half(book_v));
-  __syncthreads();
-  const bool halved = read_flag(big_flags, kRWaves);
-  if (halved) {
-    const uint4 hv = hhalf8(book_v);
-    if (tid < 512) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint4 *>(table + tc * 256 + tm * 128 + ((j + tid) & 7) * 16) = hv;
-    }
-    __syncthreads();
-  }
+  lds_wait_count(&sy[2], (uint32_t)kRWaves);
+  const bool halved = lds_read_word(&sy[0]) != 0u;
   const float total_mul = halved ? 2.0f : 1.0f;
 
   // this lane's activation fragments, the same for every row (kept in
@@ -588,6 +606,7 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
             bb[u] = *reinterpret_cast<const uint4 *>(
                 xs + rows_x_off(lane_g + (uint32_t)(p * kRGroups + s)));
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const half8_t wv = __builtin_bit_cast(half8_t, hadd8(a0[u], a1[u]));
@@ -613,17 +632,23 @@ __global__ __launch_bounds__(kRThreads) void gemv_2x8_rows_kernel(RowsGroup G) {
   };
 
   // rows k, k + 1, ...: row k's codes are in ring slot k % RD, refilled with
-  // row k + RD once its total is taken
+  // row k + RD once its total is taken. Every slot issues the same vector
+  // memory operations whether or not its row exists (loads past the
+  // wavefront's rows and the result store of every lane but 63 fall out of
+  // range), so the compiler can count them exactly and a row waits only for
+  // its own codes, not for the whole ring.
+  const Rsrc ry = make_rsrc(L.y, (uint32_t)L.out * 2u);
   for (int k0 = 0; k0 < nrows; k0 += RD) {
 #pragma unroll
     for (int u = 0; u < RD; ++u) {
-      if (k0 + u < nrows) {
-        const float v = row_total(cw[u]);
-        const uint32_t sc = sv[u];
-        load_row(k0 + u + RD, cw[u], sv[u]);
-        if (lane == 63)
-          L.y[r0 + wave + (k0 + u) * kRWaves] = (uint16_t)f2h((v * total_mul) * h2f(sc));
-      }
+      const int k = k0 + u;
+      float v = 0.0f;
+      if (k < nrows) v = row_total(cw[u]);
+      const uint32_t sc = sv[u];
+      load_row(k + RD, cw[u], sv[u]);
+      const uint32_t row = (uint32_t)(r0 + wave + k * kRWaves);
+      buf_store_u16(ry, (lane == 63 && k < nrows) ? row * 2u : kMOOB,
+                    (uint16_t)f2h((v * total_mul) * h2f(sc)));
     }
   }
 }
