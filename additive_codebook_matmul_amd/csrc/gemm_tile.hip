@@ -293,33 +293,67 @@ __device__ __forceinline__ void tile_multiply(const int w, const int lane, const
   // Epilogue: lane holds activation row l32 of each 32 x 32 tile; register r
   // is output row 8 (r / 4) + 4 hl + r % 4, so registers 4 q .. 4 q + 3 are
   // four consecutive rows (one 8-byte store when out is a multiple of 4).
-  const bool packed = (out & 3) == 0;
+  // The scales of the lane's sixteen groups of four rows are all loaded
+  // before the first store: stores count against the same wait counter as
+  // loads, so a scale load after a store would wait for that store too, and
+  // the stores would take one memory round trip each.
+  const Rsrc rsc = make_rsrc(scales, (uint32_t)out * 2u);
+  constexpr uint32_t kOOB = 0x80000000u;  // past the buffer: reads zero
+  auto epilogue = [&](auto packed_c) {
+    constexpr bool packed = decltype(packed_c)::value;
+    uint2 sc[4][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int tok = tok0 + w * 64 + ni * 32 + l32;
-      if (tok >= batch) continue;
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rb = row0 + mi * 32 + 8 * q + 4 * hl;
-        if (packed && rb + 3 < out) {
+        if constexpr (packed) {  // rb and out multiples of 4: the four rows are all in or all out
+          sc[mi][q] = buf_load8(rsc, rb < out ? (uint32_t)rb * 2u : kOOB);
+        } else {
           uint32_t h[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            h[e] = f2h((acc[mi][ni][4 * q + e] * total_mul) * h2f(scales[rb + e]));
-          *reinterpret_cast<uint2 *>(y + (int64_t)tok * out + rb) =
-              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        } else {
+            h[e] = buf_load_u16(rsc, rb + e < out ? (uint32_t)(rb + e) * 2u : kOOB);
+          sc[mi][q] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        }
+      }
+    auto scale_of = [&](int mi, int q, int e) {
+      const uint32_t v = (e >> 1) ? sc[mi][q].y : sc[mi][q].x;
+      return h2f((e & 1) ? v >> 16 : v & 0xFFFFu);
+    };
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (rb + e < out)
-              y[(int64_t)tok * out + rb + e] =
-                  (uint16_t)f2h((acc[mi][ni][4 * q + e] * total_mul) * h2f(scales[rb + e]));
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int tok = tok0 + w * 64 + ni * 32 + l32;
+        if (tok >= batch) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rb = row0 + mi * 32 + 8 * q + 4 * hl;
+          if constexpr (packed) {
+            if (rb < out) {
+              uint32_t h[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                h[e] = f2h((acc[mi][ni][4 * q + e] * total_mul) * scale_of(mi, q, e));
+              *reinterpret_cast<uint2 *>(y + (int64_t)tok * out + rb) =
+                  make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (rb + e < out)
+                y[(int64_t)tok * out + rb + e] =
+                    (uint16_t)f2h((acc[mi][ni][4 * q + e] * total_mul) * scale_of(mi, q, e));
+          }
         }
       }
     }
-  }
+  };
+  if ((out & 3) == 0)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 template <Scheme S>
