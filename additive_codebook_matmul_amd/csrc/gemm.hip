@@ -277,7 +277,18 @@ __global__ __launch_bounds__(kBlock) void gemm_wide_kernel(
   if (kb + 2 < nkb) iter(kb + 2, std::integral_constant<int, 2>{});
 
   // Epilogue: lane holds column l32 of each 32x32 tile; register r is row
-  // 8*(r/4) + 4*half + r%4.
+  // 8*(r/4) + 4*half + r%4. The lane's 32 row scales are loaded before the
+  // first store: stores count against the same wait counter as loads, so a
+  // scale load after a store would wait for that store.
+  const Rsrc rsc = make_rsrc(scales, (uint32_t)out * 2u);
+  uint32_t sh[2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      sh[mi][r] = buf_load_u16(rsc, row < out ? (uint32_t)row * 2u : kWideOOB);
+    }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kBlock) void gemm_wide_kernel(
         const int row = row0 + mi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         if (row < out)
           y[(int64_t)tok * out + row] =
-              (uint16_t)f2h((acc[mi][ni][r] * total_mul) * h2f(scales[row]));
+              (uint16_t)f2h((acc[mi][ni][r] * total_mul) * h2f(sh[mi][r]));
       }
     }
   }
@@ -567,20 +578,30 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void gemm_skinny_kernel(
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = acc[t] * 2.0f;
   }
-  // Epilogue: add the waves' partial sums in wave order, scale, round.
-  auto write = [&](int t, int l, const float4_t &v) {
+  // Epilogue: add the waves' partial sums in wave order, scale, round. The
+  // rows of an element depend on its lane only; their scales are loaded
+  // before its stores (stores count against the same wait counter as loads).
+  const Rsrc rsc = make_rsrc(scales, (uint32_t)out * 2u);
+  auto row_scales = [&](int l, uint32_t (&sh)[4]) {
+    const int rb = row0 + 4 * (l >> 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sh[k] = buf_load_u16(rsc, rb + k < out ? (uint32_t)(rb + k) * 2u : kWideOOB);
+  };
+  auto write = [&](int t, int l, const float4_t &v, const uint32_t (&sh)[4]) {
     const int tok = tok0 + 16 * t + (l & 15);
     if (tok >= batch) return;
     const int rb = row0 + 4 * (l >> 4);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int row = rb + k;
-      if (row < out) y[(int64_t)tok * out + row] = (uint16_t)f2h(v[k] * h2f(scales[row]));
+      if (row < out) y[(int64_t)tok * out + row] = (uint16_t)f2h(v[k] * h2f(sh[k]));
     }
   };
   if (waves == 1) {
+    uint32_t sh[4];
+    row_scales(lane, sh);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) write(t, lane, acc[t]);
+    for (int t = 0; t < NT; ++t) write(t, lane, acc[t], sh);
     return;
   }
   float4_t *red = reinterpret_cast<float4_t *>(lds_xall);
@@ -592,7 +613,9 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWaves) void gemm_skinny_kernel(
     const int t = e >> 6, l = e & 63;
     float4_t v = red[t * 64 + l];
     for (int w = 1; w < waves; ++w) v += red[(w * NT + t) * 64 + l];
-    write(t, l, v);
+    uint32_t sh[4];
+    row_scales(l, sh);
+    write(t, l, v, sh);
   }
 }
 
